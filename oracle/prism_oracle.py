@@ -1,0 +1,300 @@
+"""Plain float64 CPU oracle for Prism's spectral-aware block-importance
+estimator and for the block-sparse causal attention that consumes its mask.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this module. It shares no code with the HIP path
+(it imports nothing from it), and the HIP path never calls it.
+
+Sources (web pages about "Prism: Spectral-Aware Block-Sparse Attention",
+arXiv 2602.08426):
+  * Prism review, paper.rainbus.top -- the pipeline paragraph lists the seven
+    steps (1) spectral slicing ... (7) mask union; the novelty paragraph gives
+    the pooling decay lambda_j(B) ~ sinc(B*theta_j/2pi) and says the
+    calibration is RMS-energy based with no hyperparameters; the
+    reproducibility paragraph gives B=128, d_high=64, d_low=96, p=0.95/0.93.
+  * gist.science explainer, Technical Summary section 2 (dual-band estimation;
+    RMS of the pooled representations gives tau_high, tau_low) and section 1
+    (block-sparse attention computes only the selected blocks).
+  * Abstract (insight.artgrammer.co.kr / newx.sg / fugumt.com): block-sparse
+    attention for long-context pre-filling, estimation from purely block-level
+    operations.
+
+Every function works in float64 on values widened exactly from the bytes the
+GPU reads. Readings taken where the pages are silent:
+  * bands are RoPE frequency bands: 'interleaved' layout -> the literal
+    first d_high / last d_low dims; 'half' layout -> the same frequency pairs;
+  * RMS is taken over all pooled blocks of a head, per tensor and per band;
+  * tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full))
+    (the formula is named but not printed) -- parity unpinned against the
+    pages; tau = 1 if any R is 0;
+  * causal softmax over key blocks j <= i; Top-P keeps the smallest set of
+    highest scores whose mass reaches p (inclusive), ties by lower index;
+  * attention scale 1/sqrt(d); a query with no admissible key outputs 0;
+  * a partial last block averages the tokens it holds.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROPE_LAYOUTS = ("interleaved", "half")
+TAU_MODES = ("fullspec", "none")
+
+
+# ---------------------------------------------------------------- step (1)
+def band_dims(d: int, d_high: int, d_low: int, rope_layout: str = "interleaved"):
+    """Index sets of the high band, the low band and the full spectrum.
+
+    Prism review (paper.rainbus.top), pipeline step (1): Q and K are cut into
+    a high band (the first d_high dims) and a low band (the last d_low dims).
+    gist.science Technical Summary 2A: the high branch isolates the dims that
+    carry fine relative position, the low branch the semantic dims.
+    With interleaved RoPE (pair j = dims 2j, 2j+1, frequency falling with j)
+    these are literally dims [0, d_high) and [d - d_low, d). With the
+    rotate-half layout (pair j = dims j, j + d/2) the same frequency pairs are
+    {j, j+d/2 : j < d_high/2} and {j, j+d/2 : j >= d/2 - d_low/2}.
+    """
+    if rope_layout == "interleaved":
+        hi = np.arange(0, d_high)
+        lo = np.arange(d - d_low, d)
+    elif rope_layout == "half":
+        h = d // 2
+        hp = np.arange(0, d_high // 2)
+        lp = np.arange(h - d_low // 2, h)
+        hi = np.sort(np.concatenate([hp, hp + h]))
+        lo = np.sort(np.concatenate([lp, lp + h]))
+    else:
+        raise ValueError(rope_layout)
+    return hi, lo, np.arange(d)
+
+
+# ---------------------------------------------------------------- step (2)
+def mean_pool(x: np.ndarray, block: int) -> np.ndarray:
+    """Mean over each block of `block` tokens: x [N, d] -> [ceil(N/B), d].
+
+    Prism review, pipeline step (2): each band is mean-pooled over blocks of
+    size B independently. Pooling all d dims once and taking the bands as
+    index subsets afterwards gives the same numbers. Block i holds tokens
+    [iB, min((i+1)B, N)); a partial last block averages the tokens it holds.
+    """
+    N, d = x.shape
+    nb = -(-N // block)
+    out = np.empty((nb, d), dtype=np.float64)
+    for i in range(nb):
+        out[i] = x[i * block: min((i + 1) * block, N)].mean(axis=0)
+    return out
+
+
+# ---------------------------------------------------------------- step (3)
+def band_rms(xbar: np.ndarray, dims: np.ndarray) -> float:
+    """RMS energy of a pooled band: sqrt(mean over blocks i, dims c in D of xbar[i,c]^2).
+
+    Prism review, pipeline step (3): the RMS of each pooled band measures its
+    spectral energy density. gist.science Technical Summary 2B: the RMS of the
+    pooled representations.
+    """
+    return float(np.sqrt(np.mean(xbar[:, dims] ** 2)))
+
+
+# ---------------------------------------------------------------- step (4)
+def temperature(qbar: np.ndarray, kbar: np.ndarray, dims_z: np.ndarray, dims_full: np.ndarray,
+                mode: str = "fullspec") -> tuple[float, bool]:
+    """Branch temperature tau_z and whether the degenerate fallback was used.
+
+    Prism review, pipeline step (4): a per-branch temperature tau_z aligns the
+    branch's logit magnitude with the full spectrum; novelty paragraph: it is
+    RMS-energy based and has no hyperparameters; gist.science 2B: computed
+    from the RMS of the pooled representations. The formula itself is not
+    printed; the reading used here is the band's pooled energy relative to the
+    full spectrum's, for query and key:
+        tau_z = R(Qbar, D_z) R(Kbar, D_z) / (R(Qbar, D_full) R(Kbar, D_full)).
+    mode 'none' gives tau = 1 (plain pooled scores per band).
+    """
+    if mode == "none":
+        return 1.0, False
+    if mode != "fullspec":
+        raise ValueError(mode)
+    rq_z, rk_z = band_rms(qbar, dims_z), band_rms(kbar, dims_z)
+    rq_f, rk_f = band_rms(qbar, dims_full), band_rms(kbar, dims_full)
+    if min(rq_z, rk_z, rq_f, rk_f) == 0.0:
+        return 1.0, True
+    return (rq_z * rk_z) / (rq_f * rk_f), False
+
+
+# ---------------------------------------------------------------- step (5)
+def admissible(i: int, nb: int, causal: bool) -> np.ndarray:
+    """Key blocks a query block may score: j <= i under causal prefill."""
+    return np.arange(i + 1) if causal else np.arange(nb)
+
+
+def band_scores(qbar: np.ndarray, kbar: np.ndarray, dims_z: np.ndarray, tau: float,
+                causal: bool) -> tuple[np.ndarray, np.ndarray]:
+    """Logits L and block softmax S of one branch.
+
+    Prism review, pipeline step (5):
+        S_z = softmax(Qbar_z Kbar_z^T / (tau_z sqrt(d_z))),
+    the softmax of row i taken over the admissible key blocks J(i) (j <= i when
+    causal). Entries outside J(i): L = -inf, S = 0.
+    """
+    nb = qbar.shape[0]
+    L = (qbar[:, dims_z] @ kbar[:, dims_z].T) / (tau * np.sqrt(len(dims_z)))
+    S = np.zeros_like(L)
+    Lm = np.full_like(L, -np.inf)
+    for i in range(nb):
+        J = admissible(i, nb, causal)
+        row = L[i, J]
+        e = np.exp(row - row.max())
+        S[i, J] = e / e.sum()
+        Lm[i, J] = row
+    return Lm, S
+
+
+# ---------------------------------------------------------------- step (6)
+def top_p(scores: np.ndarray, p: float) -> np.ndarray:
+    """Top-P over one row's admissible scores; returns a boolean selection.
+
+    Prism review, pipeline step (6): each branch keeps, per query block, the
+    blocks chosen by Top-P. Read as: sort descending (equal scores by lower
+    block index first), keep the shortest prefix whose cumulative mass is
+    >= p (all of them if the mass never reaches p, and all if p >= 1).
+    """
+    n = scores.shape[0]
+    sel = np.zeros(n, dtype=bool)
+    if n == 0:
+        return sel
+    if p >= 1.0:
+        sel[:] = True
+        return sel
+    order = np.argsort(-scores, kind="stable")
+    cum = np.cumsum(scores[order])
+    reach = np.flatnonzero(cum >= p)
+    k = reach[0] + 1 if reach.size else n
+    sel[order[:k]] = True
+    return sel
+
+
+def top_p_mask(S: np.ndarray, p: float, causal: bool) -> np.ndarray:
+    """Apply top_p to every row of a branch's score matrix over J(i)."""
+    nb = S.shape[0]
+    M = np.zeros(S.shape, dtype=np.uint8)
+    for i in range(nb):
+        J = admissible(i, nb, causal)
+        M[i, J[top_p(S[i, J], p)]] = 1
+    return M
+
+
+# ---------------------------------------------------------------- step (7)
+def union(m_high: np.ndarray, m_low: np.ndarray) -> np.ndarray:
+    """Prism review, pipeline step (7): the final block mask is M_high OR M_low."""
+    return (m_high.astype(bool) | m_low.astype(bool)).astype(np.uint8)
+
+
+# ------------------------------------------------------- steps (1)-(7) together
+def estimate_head(qh: np.ndarray, kg: np.ndarray, *, block: int, d_high: int, d_low: int, p: float,
+                  causal: bool = True, rope_layout: str = "interleaved", tau_mode: str = "fullspec",
+                  kbar: np.ndarray | None = None) -> dict:
+    """The estimator for one query head: qh [N, d], kg [N, d] (its KV head)."""
+    d = qh.shape[1]
+    hi, lo, full = band_dims(d, d_high, d_low, rope_layout)
+    qbar = mean_pool(qh, block)
+    if kbar is None:
+        kbar = mean_pool(kg, block)
+    tau_h, deg_h = temperature(qbar, kbar, hi, full, tau_mode)
+    tau_l, deg_l = temperature(qbar, kbar, lo, full, tau_mode)
+    L_h, S_h = band_scores(qbar, kbar, hi, tau_h, causal)
+    L_l, S_l = band_scores(qbar, kbar, lo, tau_l, causal)
+    m_h = top_p_mask(S_h, p, causal)
+    m_l = top_p_mask(S_l, p, causal)
+    return {
+        "qbar": qbar, "kbar": kbar,
+        "rms_q": (band_rms(qbar, hi), band_rms(qbar, lo), band_rms(qbar, full)),
+        "rms_k": (band_rms(kbar, hi), band_rms(kbar, lo), band_rms(kbar, full)),
+        "tau": (tau_h, tau_l), "degenerate": int(deg_h) + int(deg_l),
+        "L_high": L_h, "L_low": L_l, "S_high": S_h, "S_low": S_l,
+        "m_high": m_h, "m_low": m_l, "mask": union(m_h, m_l),
+    }
+
+
+def estimate(q: np.ndarray, k: np.ndarray, *, block: int, d_high: int, d_low: int, p: float,
+             causal: bool = True, rope_layout: str = "interleaved", tau_mode: str = "fullspec",
+             heads=None, keep=False) -> dict:
+    """Estimator over q [b, N, Hq, d], k [b, N, Hkv, d] (float64, BSHD).
+
+    Query head h reads KV head h // (Hq/Hkv) (grouped-query attention).
+    Returns mask [b, Hq, nb, nb] (uint8), tau [b, Hq, 2], and, with keep=True,
+    the per-head intermediate dicts.
+    """
+    b, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq % Hkv != 0")
+    G = Hq // Hkv
+    nb = -(-N // block)
+    heads = range(Hq) if heads is None else heads
+    mask = np.zeros((b, Hq, nb, nb), dtype=np.uint8)
+    tau = np.zeros((b, Hq, 2))
+    per = {}
+    kbars = {}
+    for bb in range(b):
+        for h in heads:
+            g = h // G
+            if (bb, g) not in kbars:
+                kbars[(bb, g)] = mean_pool(k[bb, :, g, :], block)
+            r = estimate_head(q[bb, :, h, :], k[bb, :, g, :], block=block, d_high=d_high, d_low=d_low,
+                              p=p, causal=causal, rope_layout=rope_layout, tau_mode=tau_mode,
+                              kbar=kbars[(bb, g)])
+            mask[bb, h] = r["mask"]
+            tau[bb, h] = r["tau"]
+            if keep:
+                per[(bb, h)] = r
+    return {"mask": mask, "tau": tau, "per_head": per}
+
+
+# ------------------------------------------------------ block-sparse attention
+def attention_block_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask_row: np.ndarray, i: int, *,
+                        block: int, causal: bool) -> np.ndarray:
+    """Output rows of query block i for one head: q,k,v [N, d] -> [n_i, d].
+
+    Block-sparse prefill (abstract; gist.science Technical Summary section 1):
+    query t of block i attends to the keys s of the selected key blocks
+    (mask_row[s // B] == 1) with s <= t when causal, by a softmax of
+    q_t . k_s / sqrt(d); a query with no admissible key outputs 0.
+    """
+    N, d = q.shape
+    t0, t1 = i * block, min((i + 1) * block, N)
+    sel = np.flatnonzero(mask_row)
+    if sel.size == 0:
+        return np.zeros((t1 - t0, v.shape[1]))
+    keys = np.concatenate([np.arange(j * block, min((j + 1) * block, N)) for j in sel])
+    logits = (q[t0:t1] @ k[keys].T) / np.sqrt(d)
+    if causal:
+        logits = np.where(keys[None, :] <= np.arange(t0, t1)[:, None], logits, -np.inf)
+    out = np.zeros((t1 - t0, v.shape[1]))
+    for r in range(t1 - t0):
+        row = logits[r]
+        if not np.isfinite(row).any():
+            continue
+        w = np.exp(row - row.max())
+        out[r] = (w / w.sum()) @ v[keys]
+    return out
+
+
+def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, *, block: int,
+                           causal: bool = True, rows=None) -> np.ndarray:
+    """O [b, N, Hq, dv] for q [b, N, Hq, d], k/v [b, N, Hkv, d], mask [b, Hq, nb, nb].
+
+    rows: optional iterable of (b, h, i) query blocks to compute; the others
+    stay NaN (so a sampled comparison can only read what was computed).
+    """
+    b, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    nb = -(-N // block)
+    out = np.full((b, N, Hq, v.shape[3]), np.nan)
+    if rows is None:
+        rows = [(bb, h, i) for bb in range(b) for h in range(Hq) for i in range(nb)]
+    for bb, h, i in rows:
+        g = h // G
+        out[bb, i * block: min((i + 1) * block, N), h, :] = attention_block_row(
+            q[bb, :, h, :], k[bb, :, g, :], v[bb, :, g, :], mask[bb, h, i], i, block=block, causal=causal)
+    return out
+

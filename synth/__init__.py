@@ -1,0 +1,6 @@
+"""Seeded synthetic workloads (inputs only; no estimator or attention arithmetic)."""
+from .gen import (WORKLOADS, Workload, apply_rope, bf16_bits_to_f32, f32_to_bf16_bits,
+                  make_qkv, random_mask, rope_tables, to_f64)
+
+__all__ = ["WORKLOADS", "Workload", "apply_rope", "bf16_bits_to_f32", "f32_to_bf16_bits",
+           "make_qkv", "random_mask", "rope_tables", "to_f64"]

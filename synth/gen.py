@@ -1,0 +1,223 @@
+"""Seeded synthetic inputs for the Prism estimator and block-sparse prefill.
+
+This module builds inputs only. It holds none of the estimator's or the
+attention's arithmetic (no pooling, RMS, temperature, softmax, Top-P or
+attention), so both the HIP path and the CPU oracle may take their inputs
+from it.
+
+Post-RoPE Q and K are made the way a prefill layer would see them: a
+pre-rotation vector per token, rotated by the standard rotary embedding
+(pair j turns by angle t * theta_j at position t, theta_j = base^(-2j/d)).
+The Prism pages name RoPE as the source of the high/low frequency split
+(Prism review on paper.rainbus.top, novelty paragraph; gist.science
+Technical Summary, section 1) but print no formula, so the RoFormer form is
+used. Angles are computed in float64.
+
+Every value is generated in float32, rotated in float64, rounded to float32
+(round-to-nearest-even) and then, for bf16 workloads, to bfloat16
+(round-to-nearest-even). The same bytes go to the GPU and to the oracle.
+
+Seeds: one numpy PCG64 stream per (workload seed, tensor, head, batch), via
+``np.random.default_rng([seed, tensor_id, head, batch])``.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+# tensor ids for seeding
+T_QNOISE, T_KNOISE, T_V, T_SEMANTIC, T_SLASH = 0, 1, 2, 3, 4
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic attention-layer workload."""
+
+    name: str
+    seed: int
+    batch: int
+    seq: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str  # "bf16" or "fp32"
+    theta: float  # RoPE base
+    kind: str  # "iid" (Q,K,V ~ N(0,1)) or "semantic" (0.7*s + 0.7*z)
+    planted: bool  # slash + vertical structure planted in K
+    p: float
+    block: int = 128
+    d_high: int = 64
+    d_low: int = 96
+    causal: bool = True
+
+    @property
+    def nb(self) -> int:
+        return -(-self.seq // self.block)
+
+    def scaled(self, **kw) -> "Workload":
+        """Same recipe at other sizes (the seed is kept unless given)."""
+        return replace(self, **kw)
+
+
+# The five workloads: Prism's hyperparameters B=128, d_high=64, d_low=96,
+# p=0.95 (Llama) / 0.93 (Qwen) from the Prism review's reproducibility
+# paragraph (paper.rainbus.top); model shapes are Llama-3-8B, Qwen3-8B and a
+# one-GPU share of Llama-3-70B attention layers at 32K-128K tokens.
+WORKLOADS = {
+    "tiny_fp32_2k": Workload("tiny_fp32_2k", 1, 1, 2048, 1, 1, 128, "fp32", 1e4, "iid", False, 0.95),
+    "llama3_8b_32k": Workload("llama3_8b_32k", 2, 1, 32768, 32, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
+    "llama3_8b_128k": Workload("llama3_8b_128k", 3, 1, 131072, 32, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
+    "qwen3_8b_64k": Workload("qwen3_8b_64k", 4, 1, 65536, 32, 8, 128, "bf16", 1e6, "semantic", True, 0.93),
+    "llama3_70b_share_128k": Workload("llama3_70b_share_128k", 5, 1, 131072, 64, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
+}
+
+
+def _rng(seed: int, tensor_id: int, head: int, batch: int) -> np.random.Generator:
+    return np.random.default_rng([seed, tensor_id, head, batch])
+
+
+def rope_tables(seq: int, d: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin of t*theta_j for t < seq, j < d/2, in float64."""
+    j = np.arange(d // 2, dtype=np.float64)
+    freq = theta ** (-2.0 * j / d)
+    ang = np.arange(seq, dtype=np.float64)[:, None] * freq[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, layout: str) -> np.ndarray:
+    """Rotate x [seq, d] (float64). 'interleaved' pairs dims (2j, 2j+1); 'half'
+    pairs dims (j, j + d/2) (the rotate-half convention)."""
+    d = x.shape[-1]
+    if layout == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+    elif layout == "half":
+        a, b = x[..., : d // 2], x[..., d // 2:]
+    else:
+        raise ValueError(layout)
+    ra = a * cos - b * sin
+    rb = a * sin + b * cos
+    out = np.empty_like(x)
+    if layout == "interleaved":
+        out[..., 0::2], out[..., 1::2] = ra, rb
+    else:
+        out[..., : d // 2], out[..., d // 2:] = ra, rb
+    return out
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    x32 = x64.astype(np.float32)
+    return f32_to_bf16_bits(x32) if dtype == "bf16" else x32
+
+
+def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits_to_f32(x).astype(np.float64) if dtype == "bf16" else x.astype(np.float64)
+
+
+def _workers() -> int:
+    return max(1, min(8, os.cpu_count() or 1))
+
+
+def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True):
+    """Q [b, N, Hq, d], K [b, N, Hkv, d], V [b, N, Hkv, d] in BSHD order.
+
+    bf16 workloads return uint16 bit patterns, fp32 workloads float32.
+    Recipes:
+      iid:      Q, K = RoPE(z), z ~ N(0,1) per token; V ~ N(0,1).
+      semantic: Q_h = RoPE(0.7*s_g(h) + 0.7*z), K_g = RoPE(0.7*s_g + 0.7*z'),
+                s_g ~ N(0,1)^d fixed per KV group g and shared by the group's
+                query heads; V ~ N(0,1).
+      planted (on top of semantic, on post-RoPE K of each KV group g):
+        slash:    K_g[n] += 0.5 * mean_{h in g} Q_h[n + delta_n],
+                  delta_n ~ U{1..4} per key (skipped past the end);
+        vertical: K_g[n] += 1.0 * mean_{t, h in g} Q_h[t] for n % 4096 == 0.
+    """
+    b, N, Hq, Hkv, d = w.batch, w.seq, w.hq, w.hkv, w.head_dim
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    cos, sin = rope_tables(N, d, w.theta)
+    st = np.uint16 if w.dtype == "bf16" else np.float32
+    q = np.empty((b, N, Hq, d), st)
+    k = np.empty((b, N, Hkv, d), st)
+    v = np.empty((b, N, Hkv, d), st) if with_v else None
+
+    def semantic(bb, g):
+        return _rng(w.seed, T_SEMANTIC, g, bb).standard_normal(d, dtype=np.float32).astype(np.float64)
+
+    def pre(bb, tensor_id, head, g):
+        z = _rng(w.seed, tensor_id, head, bb).standard_normal((N, d), dtype=np.float32).astype(np.float64)
+        if w.kind == "semantic":
+            return 0.7 * semantic(bb, g)[None, :] + 0.7 * z
+        return z
+
+    def do_q(args):
+        bb, h = args
+        q[bb, :, h, :] = _store(apply_rope(pre(bb, T_QNOISE, h, h // G), cos, sin, rope_layout), w.dtype)
+
+    def do_k(args):
+        bb, g = args
+        kk = apply_rope(pre(bb, T_KNOISE, g, g), cos, sin, rope_layout)
+        if w.planted:
+            qg = _widen(q[bb, :, g * G:(g + 1) * G, :], w.dtype).mean(axis=1)  # [N, d]
+            delta = _rng(w.seed, T_SLASH, g, bb).integers(1, 5, size=N)
+            src = np.arange(N) + delta
+            ok = src < N
+            kk[ok] += 0.5 * qg[src[ok]]
+            kk[0::4096] += 1.0 * qg.mean(axis=0)[None, :]
+        k[bb, :, g, :] = _store(kk, w.dtype)
+
+    def do_v(args):
+        bb, g = args
+        z = _rng(w.seed, T_V, g, bb).standard_normal((N, d), dtype=np.float32)
+        v[bb, :, g, :] = f32_to_bf16_bits(z) if w.dtype == "bf16" else z
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(do_q, [(bb, h) for bb in range(b) for h in range(Hq)]))
+        list(ex.map(do_k, [(bb, g) for bb in range(b) for g in range(Hkv)]))
+        if with_v:
+            list(ex.map(do_v, [(bb, g) for bb in range(b) for g in range(Hkv)]))
+    return q, k, v
+
+
+def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Widen stored values (bf16 bits or float32) to float64, exactly."""
+    return _widen(x, dtype)
+
+
+def random_mask(batch: int, heads: int, nb: int, density: float, seed: int, causal: bool = True) -> np.ndarray:
+    """A seeded uint8 block mask [b, H, nb, nb] (1 = compute) for attention tests."""
+    rng = np.random.default_rng([seed, 99])
+    m = (rng.random((batch, heads, nb, nb)) < density).astype(np.uint8)
+    if causal:
+        m *= np.tril(np.ones((nb, nb), np.uint8))[None, None]
+    return m
+
+
+def planted_blocks(w: Workload) -> dict:
+    """Block coordinates of the planted structure (for recall reports)."""
+    B = w.block
+    return {
+        "slash_offsets": (1, 4),
+        "vertical_key_blocks": sorted({n // B for n in range(0, w.seq, 4096)}),
+    }
+
+
+__all__ = [
+    "Workload", "WORKLOADS", "make_qkv", "rope_tables", "apply_rope", "f32_to_bf16_bits",
+    "bf16_bits_to_f32", "to_f64", "random_mask", "planted_blocks",
+]

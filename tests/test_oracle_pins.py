@@ -1,0 +1,421 @@
+"""Pins of the CPU oracle to facts fixed by the Prism pages and by mathematics.
+
+Each check is written as a function that returns an error measure, so the
+planted-mistake tests at the bottom can show that a plausible slip in the
+oracle (swapped bands, a dropped scale, a strict inequality, a missing causal
+mask) makes a pin fail.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle.prism_oracle as po
+from synth import WORKLOADS, apply_rope, rope_tables
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, val = line.split()
+                vals[key] = float(val)
+    return vals
+
+
+def dirichlet(B, theta):
+    """|mean_{m<B} exp(i m theta)| = |sin(B theta/2) / (B sin(theta/2))|, signed."""
+    return np.sin(B * theta / 2) / (B * np.sin(theta / 2))
+
+
+def freqs(d, base):
+    return base ** (-2.0 * np.arange(d // 2) / d)
+
+
+# --------------------------------------------------------------- golden values
+def test_hyperparameters_match_pages():
+    g = read_golden("prism_hyperparameters.txt")
+    for name, w in WORKLOADS.items():
+        assert w.block == g["block_size"] and w.d_high == g["d_high"] and w.d_low == g["d_low"], name
+        assert w.p == (g["p_qwen"] if name.startswith("qwen") else g["p_llama"]), name
+
+
+# ------------------------------------------- pin 1: pooling under RoPE (closed form)
+def pooling_decay_error(base, B=128, d=128, block_index=3):
+    """Pool RoPE-rotated unit pairs over one block and compare the pooled pair
+    with the closed form: amplitude D_B(theta_j), phase at the block centre.
+    Returns (max err vs Dirichlet form, max err of |pooled| vs |sinc|)."""
+    N = (block_index + 1) * B
+    cos, sin = rope_tables(N, d, base)
+    x = np.zeros((N, d))
+    x[:, 0::2] = 1.0  # every pair starts as the unit vector (1, 0)
+    xr = apply_rope(x, cos, sin, "interleaved")
+    pooled = po.mean_pool(xr, B)[block_index]
+    th = freqs(d, base)
+    centre = block_index * B + (B - 1) / 2.0
+    amp = dirichlet(B, th)
+    expect = np.empty(d)
+    expect[0::2] = amp * np.cos(centre * th)
+    expect[1::2] = amp * np.sin(centre * th)
+    err_exact = np.abs(pooled - expect).max()
+    lam = np.hypot(pooled[0::2], pooled[1::2])
+    # the pages' closed form: lambda_j(B) ~ sinc(B theta_j / 2 pi) (normalised sinc)
+    err_sinc = np.abs(lam - np.abs(np.sinc(B * th / (2 * np.pi)))).max()
+    return err_exact, err_sinc
+
+
+@pytest.mark.parametrize("base", [1e4, 5e5, 1e6])
+def test_pooling_is_lowpass_sinc(base):
+    """Prism review, novelty paragraph: mean pooling under RoPE attenuates pair j
+    by lambda_j(B) ~ sinc(B theta_j / 2 pi)."""
+    e_exact, e_sinc = pooling_decay_error(base)
+    assert e_exact < 1e-12
+    assert e_sinc < 1e-3
+
+
+def test_pooling_dead_zone():
+    """gist.science Technical Summary 1: the fastest-rotating pairs collapse to
+    near zero after pooling, the slowest pass through."""
+    th = freqs(128, 5e5)
+    lam = np.abs(dirichlet(128, th))
+    assert lam[:8].max() < 0.05 and lam[-4:].min() > 0.99
+
+
+# --------------------------------- pin 2: RMS and temperature (closed form)
+def tau_closed_form_error(rope_layout, d_high, d_low, base=5e5, B=64, nb=5, seed=0):
+    """Q = K = RoPE(x) for a constant pre-rotation x over full blocks: each pair's
+    pooled energy is D_B(theta_j)^2 |x_j|^2 in every block, so
+    tau_z = [sum_{j in F_z} D^2 |x_j|^2 / |D_z|] / [sum_j D^2 |x_j|^2 / d]."""
+    d = 128
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(d)
+    N = nb * B
+    cos, sin = rope_tables(N, d, base)
+    xr = apply_rope(np.tile(x, (N, 1)), cos, sin, rope_layout)
+    r = po.estimate_head(xr, xr, block=B, d_high=d_high, d_low=d_low, p=0.9, rope_layout=rope_layout)
+    D2 = dirichlet(B, freqs(d, base)) ** 2
+    if rope_layout == "interleaved":
+        e = x[0::2] ** 2 + x[1::2] ** 2
+    else:
+        e = x[: d // 2] ** 2 + x[d // 2:] ** 2
+    pair = D2 * e
+    F_hi = np.arange(0, d_high // 2)
+    F_lo = np.arange(d // 2 - d_low // 2, d // 2)
+    full = pair.sum() / d
+    t_hi = (pair[F_hi].sum() / (2 * len(F_hi))) / full
+    t_lo = (pair[F_lo].sum() / (2 * len(F_lo))) / full
+    r_hi = math.sqrt(pair[F_hi].sum() / (2 * len(F_hi)))
+    rel = lambda a, b: abs(a - b) / abs(b)
+    return max(rel(r["tau"][0], t_hi), rel(r["tau"][1], t_lo), rel(r["rms_q"][0], r_hi),
+               rel(r["rms_k"][2], math.sqrt(full)))
+
+
+@pytest.mark.parametrize("rope_layout", ["interleaved", "half"])
+@pytest.mark.parametrize("d_high,d_low", [(64, 96), (32, 112), (48, 48), (128, 128)])
+def test_tau_closed_form(rope_layout, d_high, d_low):
+    assert tau_closed_form_error(rope_layout, d_high, d_low) < 1e-12
+
+
+def test_tau_attenuated_high_band_is_amplified():
+    """gist.science 2B: the high branch's pooled logits are attenuated, and the
+    calibration restores them (tau_high < 1 divides the logits up)."""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=4096, hq=1, hkv=1)
+    from synth import make_qkv, to_f64
+    q, k, _ = make_qkv(w, with_v=False)
+    r = po.estimate_head(to_f64(q, w.dtype)[0, :, 0], to_f64(k, w.dtype)[0, :, 0], block=128,
+                         d_high=64, d_low=96, p=0.95)
+    assert r["tau"][0] < 1.0 < r["tau"][1]
+
+
+def test_tau_scale_invariant():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((700, 128))
+    k = rng.standard_normal((700, 128))
+    a = po.estimate_head(q, k, block=128, d_high=64, d_low=96, p=0.95)
+    b = po.estimate_head(3.7 * q, 0.2 * k, block=128, d_high=64, d_low=96, p=0.95)
+    assert np.allclose(a["tau"], b["tau"], rtol=1e-12, atol=0)
+
+
+def test_tau_degenerate_is_one():
+    q = np.zeros((256, 128))
+    k = np.ones((256, 128))
+    r = po.estimate_head(q, k, block=128, d_high=64, d_low=96, p=0.95)
+    assert r["tau"] == (1.0, 1.0) and r["degenerate"] == 2
+
+
+# --------------- special case: equal bands = plain mean-pooled block attention
+def brute_topp(s, p):
+    """Minimal-cardinality subset with mass >= p, by enumeration; returns (k, best mass set)."""
+    n = len(s)
+    for kk in range(1, n + 1):
+        best, best_set = -1.0, None
+        for c in itertools.combinations(range(n), kk):
+            m = s[list(c)].sum()
+            if m > best:
+                best, best_set = m, set(c)
+        if best >= p:
+            return kk, best_set
+    return n, set(range(n))
+
+
+def plain_pooled_error(causal, seed=2, B=16, N=139, d=128, p=0.8):
+    """d_high = d_low = d: tau = 1 and both branches equal plain pooled attention
+    softmax(Qbar Kbar^T / sqrt(d)) with Top-P, checked with scipy's softmax and
+    brute-force subset enumeration. Returns the number of violations."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((N, d)) + 0.3 * rng.standard_normal(d)
+    k = rng.standard_normal((N, d)) + 0.3 * rng.standard_normal(d)
+    r = po.estimate_head(q, k, block=B, d_high=d, d_low=d, p=p, causal=causal)
+    bad = 0
+    bad += r["tau"] != (1.0, 1.0)
+    nb = -(-N // B)
+    qb = np.stack([q[i * B:(i + 1) * B].sum(0) / len(q[i * B:(i + 1) * B]) for i in range(nb)])
+    kb = np.stack([k[i * B:(i + 1) * B].sum(0) / len(k[i * B:(i + 1) * B]) for i in range(nb)])
+    logits = np.einsum("id,jd->ij", qb, kb) / math.sqrt(d)
+    for i in range(nb):
+        J = list(range(i + 1)) if causal else list(range(nb))
+        s = scipy.special.softmax(logits[i, J])
+        bad += np.abs(r["S_high"][i, J] - s).max() > 1e-12
+        kk, best = brute_topp(s, p)
+        sel = set(np.flatnonzero(r["m_high"][i, J]).tolist())
+        bad += sel != best or len(sel) != kk
+        bad += not np.array_equal(r["m_high"][i], r["m_low"][i])
+        bad += not np.array_equal(r["mask"][i], r["m_high"][i])
+    return bad
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_equal_bands_reduce_to_plain_pooling(causal):
+    assert plain_pooled_error(causal) == 0
+
+
+# ------------------------------------------------------------- softmax rows
+def test_softmax_rows():
+    rng = np.random.default_rng(3)
+    qb, kb = rng.standard_normal((12, 128)), rng.standard_normal((12, 128))
+    hi, _, _ = po.band_dims(128, 64, 96)
+    L, S = po.band_scores(qb, kb, hi, 0.7, causal=True)
+    for i in range(12):
+        assert abs(S[i, : i + 1].sum() - 1) < 1e-14
+        assert np.all(S[i, i + 1:] == 0) and np.all(np.isneginf(L[i, i + 1:]))
+        assert np.abs(S[i, : i + 1] - scipy.special.softmax(L[i, : i + 1])).max() < 1e-15
+
+
+# ------------------------------------------------------- pin 3: Top-P invariants
+def topp_violations(trials=300, seed=4):
+    rng = np.random.default_rng(seed)
+    bad = 0
+    for _ in range(trials):
+        n = int(rng.integers(1, 11))
+        s = scipy.special.softmax(rng.standard_normal(n) * rng.uniform(0.1, 4))
+        p = float(rng.uniform(0.05, 0.999))
+        sel = po.top_p(s, p)
+        mass = s[sel].sum()
+        kk, best = brute_topp(s, p)
+        bad += sel.sum() != kk
+        bad += mass < p and sel.sum() != n
+        bad += set(np.flatnonzero(sel).tolist()) != best
+        if (~sel).any():
+            bad += s[sel].min() < s[~sel].max()
+        if sel.sum() > 1:
+            bad += mass - s[sel].min() >= p  # minimal: dropping the smallest falls short
+    return bad
+
+
+def test_top_p_bruteforce_and_invariants():
+    assert topp_violations() == 0
+
+
+def hand_topp_violations():
+    bad = 0
+    bad += not po.top_p(np.array([0.2, 0.3, 0.5]), 1.0).all()
+    bad += po.top_p(np.array([0.0, 1.0, 0.0]), 0.95).tolist() != [False, True, False]
+    for n, p in [(7, 0.95), (16, 0.95), (30, 0.95), (10, 0.93)]:
+        bad += po.top_p(np.full(n, 1.0 / n), p).sum() != math.ceil(p * n)
+    # equal scores: the lower block index goes first
+    bad += po.top_p(np.array([0.25, 0.25, 0.25, 0.25]), 0.5).tolist() != [True, True, False, False]
+    bad += po.top_p(np.array([0.1, 0.3, 0.3, 0.3]), 0.55).tolist() != [False, True, True, False]
+    return bad
+
+
+def test_top_p_hand_cases():
+    assert hand_topp_violations() == 0
+
+
+# ------------------------------------------------- pin 4: union and causality
+def small_estimate(seed=5, N=1000, B=64, causal=True):
+    rng = np.random.default_rng(seed)
+    s = rng.standard_normal(128)
+    cos, sin = rope_tables(N, 128, 1e4)
+    q = apply_rope(0.7 * s + 0.7 * rng.standard_normal((N, 128)), cos, sin, "interleaved")
+    k = apply_rope(0.7 * s + 0.7 * rng.standard_normal((N, 128)), cos, sin, "interleaved")
+    return po.estimate_head(q, k, block=B, d_high=64, d_low=96, p=0.9, causal=causal)
+
+
+def test_union_semantics():
+    r = small_estimate()
+    M, Mh, Ml = r["mask"].astype(bool), r["m_high"].astype(bool), r["m_low"].astype(bool)
+    assert (M >= Mh).all() and (M >= Ml).all() and (M <= (Mh | Ml)).all()
+    assert np.array_equal(po.union(r["m_low"], r["m_high"]), r["mask"])
+    assert (Mh != Ml).any()  # the two branches really differ on this input
+    assert M.sum(axis=1).min() >= 1  # Top-P keeps at least the argmax
+
+
+def test_mask_causal_upper_triangle_zero():
+    r = small_estimate()
+    assert not np.triu(r["mask"], 1).any()
+    r = small_estimate(causal=False)
+    assert np.triu(r["mask"], 1).any()
+
+
+def test_attention_causal_perturbation():
+    rng = np.random.default_rng(6)
+    N, B, d = 300, 64, 128
+    q, k, v = (rng.standard_normal((1, N, 1, d)) for _ in range(3))
+    nb = -(-N // B)
+    mask = np.tril(np.ones((1, 1, nb, nb), np.uint8))
+    o1 = po.block_sparse_attention(q, k, v, mask, block=B)
+    t0 = 150
+    k2, v2 = k.copy(), v.copy()
+    k2[:, t0 + 1:] = rng.standard_normal(k2[:, t0 + 1:].shape)
+    v2[:, t0 + 1:] = rng.standard_normal(v2[:, t0 + 1:].shape)
+    o2 = po.block_sparse_attention(q, k2, v2, mask, block=B)
+    assert np.array_equal(o1[:, : t0 + 1], o2[:, : t0 + 1])
+    assert not np.array_equal(o1[:, t0 + 1:], o2[:, t0 + 1:])
+
+
+# ----------------------------------------- pin 5: all blocks = dense attention
+def sdpa(q, k, v, causal, attn_mask=None):
+    """torch reference in float64 on the CPU: q [b,N,H,d], k/v [b,N,Hkv,d]."""
+    G = q.shape[2] // k.shape[2]
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=attn_mask, is_causal=causal)
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def dense_error(causal, N=333, B=64, Hq=4, Hkv=2, seed=7):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, N, Hq, 128))
+    k = rng.standard_normal((2, N, Hkv, 128))
+    v = rng.standard_normal((2, N, Hkv, 128))
+    nb = -(-N // B)
+    mask = np.ones((2, Hq, nb, nb), np.uint8)
+    o = po.block_sparse_attention(q, k, v, mask, block=B, causal=causal)
+    return np.abs(o - sdpa(q, k, v, causal)).max()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_all_blocks_equals_dense(causal):
+    assert dense_error(causal) < 1e-12
+
+
+def test_diagonal_mask_is_block_local():
+    rng = np.random.default_rng(8)
+    N, B = 300, 64
+    q, k, v = (rng.standard_normal((1, N, 1, 128)) for _ in range(3))
+    nb = -(-N // B)
+    mask = np.eye(nb, dtype=np.uint8)[None, None]
+    o = po.block_sparse_attention(q, k, v, mask, block=B, causal=True)
+    t = np.arange(N)
+    allowed = (t[None, :] // B == t[:, None] // B) & (t[None, :] <= t[:, None])
+    ref = sdpa(q, k, v, False, attn_mask=torch.from_numpy(allowed))
+    assert np.abs(o - ref).max() < 1e-12
+
+
+def test_empty_row_outputs_zero():
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((1, 256, 1, 128)) for _ in range(3))
+    mask = np.array([[[[1, 0], [0, 0]]]], np.uint8)
+    o = po.block_sparse_attention(q, k, v, mask, block=128)
+    assert np.all(o[0, 128:] == 0) and np.abs(o[0, :128]).sum() > 0
+
+
+# --------------------------------------------- planted mistakes must be caught
+def test_planted_swapped_bands_caught(monkeypatch):
+    good = po.band_dims
+
+    def swapped(d, dh, dl, layout="interleaved"):
+        hi, lo, full = good(d, dh, dl, layout)
+        return lo, hi, full
+
+    monkeypatch.setattr(po, "band_dims", swapped)
+    assert tau_closed_form_error("interleaved", 64, 96) > 1e-3
+
+
+def test_planted_rms_without_sqrt_caught(monkeypatch):
+    monkeypatch.setattr(po, "band_rms", lambda xb, dims: float(np.mean(xb[:, dims] ** 2)))
+    assert tau_closed_form_error("interleaved", 64, 96) > 1e-3
+
+
+def test_planted_inverted_tau_caught(monkeypatch):
+    good = po.temperature
+
+    def inverted(*a, **kw):
+        t, deg = good(*a, **kw)
+        return 1.0 / t, deg
+
+    monkeypatch.setattr(po, "temperature", inverted)
+    assert tau_closed_form_error("interleaved", 64, 96) > 1e-3
+
+
+def test_planted_half_layout_bands_caught(monkeypatch):
+    good = po.band_dims
+    # slicing the first d_high physical dims of a rotate-half tensor (the rejected reading)
+    monkeypatch.setattr(po, "band_dims", lambda d, dh, dl, layout="interleaved": good(d, dh, dl, "interleaved"))
+    assert tau_closed_form_error("half", 64, 96) > 1e-3
+
+
+def test_planted_missing_sqrt_d_caught(monkeypatch):
+    good = po.band_scores
+
+    def no_sqrt(qbar, kbar, dims, tau, causal):
+        return good(qbar, kbar, dims, tau / math.sqrt(len(dims)), causal)
+
+    monkeypatch.setattr(po, "band_scores", no_sqrt)
+    assert plain_pooled_error(True) > 0
+
+
+def test_planted_strict_top_p_caught(monkeypatch):
+    def strict(scores, p):
+        n = len(scores)
+        order = np.argsort(-scores, kind="stable")
+        cum = np.cumsum(scores[order])
+        reach = np.flatnonzero(cum > p)
+        kk = reach[0] + 1 if reach.size else n
+        sel = np.zeros(n, bool)
+        sel[order[:kk]] = True
+        return sel
+
+    monkeypatch.setattr(po, "top_p", strict)
+    assert hand_topp_violations() > 0
+
+
+def test_planted_missing_causal_mask_caught(monkeypatch):
+    good = po.attention_block_row
+    monkeypatch.setattr(po, "attention_block_row",
+                        lambda q, k, v, row, i, block, causal: good(q, k, v, row, i, block=block, causal=False))
+    assert dense_error(True) > 1e-3
+
+
+def test_planted_wrong_pool_divisor_caught(monkeypatch):
+    def pool_by_B(x, block):
+        N, d = x.shape
+        nb = -(-N // block)
+        out = np.zeros((nb, d))
+        for i in range(nb):
+            out[i] = x[i * block: (i + 1) * block].sum(0) / block
+        return out
+
+    monkeypatch.setattr(po, "mean_pool", pool_by_B)
+    # a ragged last block (139 = 8*16 + 11) exposes the wrong divisor
+    assert plain_pooled_error(True) > 0
