@@ -1,0 +1,127 @@
+"""Prism on MI355X: the spectral-aware block-importance estimator and the
+causal block-sparse attention prefill, as HIP kernels behind the C ABI of
+libprism.so (include/prism.h).
+
+This module only marshals arguments: it turns torch tensors (device memory on
+the current HIP stream) into the ABI's plain descriptors and calls the
+library. Every step of the path runs in the library's kernels; there is no
+fallback. Tensors are [batch, seq, heads, 128] with the last dim contiguous
+(any batch/seq/head strides), bf16 or fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+from . import _abi
+from ._abi import PrismCfg, PrismError, PrismMask, PrismTensor, PrismWorkspaceLayout, lib
+
+__all__ = ["EstimatorConfig", "estimate", "block_sparse_attn", "workspace_bytes", "workspace_layout",
+           "PrismError", "lib"]
+
+_ROPE = {"interleaved": _abi.ROPE_INTERLEAVED, "half": _abi.ROPE_HALF}
+_TAU = {"fullspec": _abi.TAU_FULLSPEC, "none": _abi.TAU_NONE}
+
+
+@dataclass(frozen=True)
+class EstimatorConfig:
+    """Prism's estimator settings (defaults: B=128, d_high=64, d_low=96, p=0.95)."""
+
+    block_size: int = 128
+    d_high: int = 64
+    d_low: int = 96
+    p: float = 0.95
+    causal: bool = True
+    rope_layout: str = "interleaved"
+    tau_mode: str = "fullspec"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _abi.BF16
+    if t.dtype == torch.float32:
+        return _abi.FP32
+    return 99  # rejected by the library with PRISM_ERR_DTYPE
+
+
+def tensor_desc(t) -> PrismTensor:
+    """Descriptor of a [batch, seq, heads, head_dim] tensor (no copy)."""
+    if t.dim() != 4:
+        raise ValueError("expected a [batch, seq, heads, head_dim] tensor")
+    if t.stride(3) != 1:
+        raise ValueError("the head_dim stride must be 1")
+    b, n, h, d = t.shape
+    sb, ss, sh, _ = t.stride()
+    return PrismTensor(t.data_ptr(), _dtype_code(t), 0, b, n, h, d, sb, ss, sh)
+
+
+def mask_desc(m, block_size: int, causal: bool) -> PrismMask:
+    torch = _torch()
+    if m.dtype != torch.uint8 or m.dim() != 4 or not m.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8 [batch, heads, nb, nb] tensor")
+    b, h, nq, nk = m.shape
+    return PrismMask(m.data_ptr(), b, h, nq, nk, block_size, int(bool(causal)))
+
+
+def _cfg(cfg: EstimatorConfig, workspace=None) -> PrismCfg:
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return PrismCfg(cfg.block_size, cfg.d_high, cfg.d_low, cfg.p, int(bool(cfg.causal)), _ROPE[cfg.rope_layout],
+                    _TAU[cfg.tau_mode], 0, ws_ptr, ws_bytes)
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def workspace_layout(q, k, cfg: EstimatorConfig = EstimatorConfig()) -> PrismWorkspaceLayout:
+    out = PrismWorkspaceLayout()
+    qd, kd, c = tensor_desc(q), tensor_desc(k), _cfg(cfg)
+    _abi.check(lib().prism_estimate_workspace_layout(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(c),
+                                                     ctypes.byref(out)), "prism_estimate_workspace_layout")
+    return out
+
+
+def workspace_bytes(q, k, cfg: EstimatorConfig = EstimatorConfig()) -> int:
+    return workspace_layout(q, k, cfg).total_bytes
+
+
+def new_workspace(q, k, cfg: EstimatorConfig = EstimatorConfig()):
+    """A device workspace of the size prism_estimate needs (torch allocation)."""
+    torch = _torch()
+    n = workspace_bytes(q, k, cfg)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def estimate(q, k, cfg: EstimatorConfig = EstimatorConfig(), *, workspace=None, mask_out=None):
+    """Prism's block mask M [batch, Hq, nb, nb] (uint8, 1 = compute) for post-RoPE q, k."""
+    torch = _torch()
+    L = workspace_layout(q, k, cfg)
+    if workspace is None:
+        workspace = torch.empty(L.total_bytes, dtype=torch.uint8, device=q.device)
+    if mask_out is None:
+        mask_out = torch.empty((q.shape[0], q.shape[2], L.nb, L.nb), dtype=torch.uint8, device=q.device)
+    qd, kd, c = tensor_desc(q), tensor_desc(k), _cfg(cfg, workspace)
+    md = mask_desc(mask_out, cfg.block_size, cfg.causal)
+    _abi.check(lib().prism_estimate(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(c), ctypes.byref(md),
+                                    ctypes.c_void_p(_stream(q))), "prism_estimate")
+    return mask_out
+
+
+def block_sparse_attn(q, k, v, mask, *, causal: bool = True, block_size: int = 128, out=None):
+    """Attention of q over the key blocks mask selects: out [batch, seq, Hq, 128]."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    qd, kd, vd, od = tensor_desc(q), tensor_desc(k), tensor_desc(v), tensor_desc(out)
+    md = mask_desc(mask, block_size, causal)
+    _abi.check(lib().prism_block_sparse_attn(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(md),
+                                             ctypes.byref(od), ctypes.c_void_p(_stream(q))), "prism_block_sparse_attn")
+    return out

@@ -1,0 +1,213 @@
+// Prism estimator, steps (1)-(4) (Prism review on paper.rainbus.top,
+// pipeline paragraph): block mean pooling of post-RoPE Q and K, the pooled
+// vectors' energy per band segment, and the per-head branch temperatures.
+//
+// pool_kernel: one streaming pass over Q and K. A workgroup owns one block of
+//   B tokens for a chunk of heads of one tensor; each thread reads 16 bytes
+//   per token (8 bf16 or 4 fp32 dims), so the workgroup's loads for a token
+//   are one contiguous run when heads are adjacent in memory (BSHD). The
+//   block sum is accumulated in fp32 in token order, divided by the number
+//   of tokens present, and written in canonical frequency order (dims 2j,
+//   2j+1 = RoPE pair j). The squares of the pooled values are summed per
+//   segment (high-only, middle, low-only) for the RMS energies.
+// tau_kernel: per query head, fixed-order fp64 sums of those segment
+//   energies over all blocks give R = sqrt(energy / (nb * |D|)) for the
+//   high band, the low band and the full spectrum of Qbar and Kbar, and
+//   tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full)).
+#include "prism_kernels.h"
+
+namespace prism {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <bool FP32>
+struct Elem;
+template <>
+struct Elem<false> {  // bf16: 8 dims per 16-byte load
+  static constexpr int E = 8;
+  static constexpr int kBytes = 2;
+  __device__ static __forceinline__ void add(float *acc, const uint4 v) {
+    acc[0] += bf16lo(v.x); acc[1] += bf16hi(v.x);
+    acc[2] += bf16lo(v.y); acc[3] += bf16hi(v.y);
+    acc[4] += bf16lo(v.z); acc[5] += bf16hi(v.z);
+    acc[6] += bf16lo(v.w); acc[7] += bf16hi(v.w);
+  }
+};
+template <>
+struct Elem<true> {  // fp32: 4 dims per 16-byte load
+  static constexpr int E = 4;
+  static constexpr int kBytes = 4;
+  __device__ static __forceinline__ void add(float *acc, const uint4 v) {
+    acc[0] += __uint_as_float(v.x); acc[1] += __uint_as_float(v.y);
+    acc[2] += __uint_as_float(v.z); acc[3] += __uint_as_float(v.w);
+  }
+};
+
+template <bool FP32>
+__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
+  using El = Elem<FP32>;
+  constexpr int E = El::E;
+  constexpr int TPH = kHeadDim / E;  // threads per head row
+  __shared__ float red[kThreads * E];
+
+  const int batch = blockIdx.y;
+  int rem = blockIdx.x;
+  int ts = 0;
+  const int nq = a.chunks[0] * a.nb;
+  if (rem >= nq) { ts = 1; rem -= nq; }
+  const int i = rem % a.nb;
+  const int chunk = rem / a.nb;
+
+  const TensorArg &x = a.x[ts];
+  const int HC = a.heads_per_chunk[ts];
+  const int lanes_per_tok = TPH * HC;
+  const int tokp = kThreads / lanes_per_tok;
+  const int tid = threadIdx.x;
+  const int tp = tid / lanes_per_tok;
+  const int hh = (tid % lanes_per_tok) / TPH;
+  const int dg = tid % TPH;
+  const int h = chunk * HC + hh;
+  const bool active = tp < tokp && h < x.heads;
+
+  const int t0 = i * a.block;
+  const int n = min(a.block, a.seq - t0);
+
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+
+  if (active) {
+    const char *base = static_cast<const char *>(x.data) +
+                       ((int64_t)batch * x.sb + (int64_t)h * x.sh + (int64_t)t0 * x.ss + dg * E) * El::kBytes;
+    const int64_t rs = x.ss * El::kBytes;
+    int t = tp;
+    for (; t + 7 * tokp < n; t += 8 * tokp) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4 *>(base + (int64_t)(t + u * tokp) * rs);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) El::add(acc, v[u]);
+    }
+    for (; t < n; t += tokp) El::add(acc, *reinterpret_cast<const uint4 *>(base + (int64_t)t * rs));
+  }
+
+  // combine the token-parallel partial sums in a fixed order
+  if (tokp > 1) {
+    if (tp < tokp) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) red[tid * E + e] = acc[e];
+    }
+    __syncthreads();
+    if (tp == 0) {
+      for (int k = 1; k < tokp; ++k) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += red[(tid + k * lanes_per_tok) * E + e];
+      }
+    }
+  }
+
+  const float inv_n = 1.0f / (float)n;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+  float mean[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    mean[e] = acc[e] * inv_n;
+    const int c = dg * E + e;  // physical dim
+    const int cc = a.half_layout ? (c < kHeadDim / 2 ? 2 * c : 2 * (c - kHeadDim / 2) + 1) : c;
+    const float sq = mean[e] * mean[e];
+    if (cc < a.seg_lo) s0 += sq;
+    else if (cc < a.seg_hi) s1 += sq;
+    else s2 += sq;
+  }
+  // sum over the TPH lanes of this head row (adjacent lanes, one wave)
+#pragma unroll
+  for (int off = TPH / 2; off >= 1; off >>= 1) {
+    s0 += __shfl_xor(s0, off, TPH);
+    s1 += __shfl_xor(s1, off, TPH);
+    s2 += __shfl_xor(s2, off, TPH);
+  }
+
+  if (active && tp == 0) {
+    const int64_t row = ((int64_t)batch * x.heads + h) * a.nb + i;
+    float *xb = a.xbar[ts] + row * kHeadDim;
+    if (!a.half_layout) {
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4 *>(xb + dg * E + e) = make_float4(mean[e], mean[e + 1], mean[e + 2], mean[e + 3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int c = dg * E + e;
+        const int cc = c < kHeadDim / 2 ? 2 * c : 2 * (c - kHeadDim / 2) + 1;
+        xb[cc] = mean[e];
+      }
+    }
+    if (dg == 0) *reinterpret_cast<float4 *>(a.sq[ts] + row * 4) = make_float4(s0, s1, s2, 0.f);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
+  __shared__ double red[6][kThreads];
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = h / (a.hq / a.hkv);
+  const float4 *qs = reinterpret_cast<const float4 *>(a.qsq) + ((int64_t)b * a.hq + h) * a.nb;
+  const float4 *ks = reinterpret_cast<const float4 *>(a.ksq) + ((int64_t)b * a.hkv + g) * a.nb;
+  double s[6] = {0, 0, 0, 0, 0, 0};
+  for (int i = threadIdx.x; i < a.nb; i += kThreads) {
+    const float4 x = qs[i];
+    const float4 y = ks[i];
+    s[0] += x.x; s[1] += x.y; s[2] += x.z;
+    s[3] += y.x; s[4] += y.y; s[5] += y.z;
+  }
+#pragma unroll
+  for (int k = 0; k < 6; ++k) red[k][threadIdx.x] = s[k];
+  __syncthreads();
+  for (int w = kThreads / 2; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double ov = a.overlap ? 1.0 : 0.0;
+    const double nb = (double)a.nb;
+    double r[6];
+    for (int t = 0; t < 2; ++t) {
+      const double e0 = red[3 * t][0], e1 = red[3 * t + 1][0], e2 = red[3 * t + 2][0];
+      r[3 * t + 0] = sqrt((e0 + ov * e1) / (nb * a.d_high));
+      r[3 * t + 1] = sqrt((e2 + ov * e1) / (nb * a.d_low));
+      r[3 * t + 2] = sqrt((e0 + e1 + e2) / (nb * kHeadDim));
+    }
+    double th = 1.0, tl = 1.0;
+    if (!a.tau_none) {
+      if (r[0] > 0 && r[3] > 0 && r[2] > 0 && r[5] > 0) th = (r[0] * r[3]) / (r[2] * r[5]);
+      if (r[1] > 0 && r[4] > 0 && r[2] > 0 && r[5] > 0) tl = (r[1] * r[4]) / (r[2] * r[5]);
+    }
+    float *out = a.tau + ((int64_t)b * a.hq + h) * 8;
+    out[0] = (float)th; out[1] = (float)tl;
+    out[2] = (float)r[0]; out[3] = (float)r[1]; out[4] = (float)r[2];
+    out[5] = (float)r[3]; out[6] = (float)r[4]; out[7] = (float)r[5];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s) {
+  const dim3 grid((a.chunks[0] + a.chunks[1]) * a.nb, batch);
+  if (fp32) hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, s, a);
+  else hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(tau_kernel, dim3(a.hq, batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace prism

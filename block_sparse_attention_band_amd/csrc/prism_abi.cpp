@@ -1,0 +1,258 @@
+// C ABI of libprism: argument validation, workspace layout and launch order.
+// Every check below runs on the host before the first HIP call of an entry
+// point; a failed check returns its status with nothing enqueued.
+#include <cmath>
+#include <cstdint>
+
+#include "prism.h"
+#include "prism_kernels.h"
+
+namespace {
+
+using prism::kBlock;
+using prism::kHeadDim;
+using prism::kMaxBlocks;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t esize(int32_t dtype) { return dtype == PRISM_BF16 ? 2 : 4; }
+
+// one [batch, seq, heads, head_dim] operand
+int check_tensor(const prism_tensor_t *t) {
+  if (!t || !t->data) return PRISM_ERR_NULL;
+  if (t->dtype != PRISM_BF16 && t->dtype != PRISM_FP32) return PRISM_ERR_DTYPE;
+  if (t->batch < 1 || t->seq < 1 || t->heads < 1 || t->head_dim < 1) return PRISM_ERR_SHAPE;
+  if (t->heads * t->batch > (1 << 20)) return PRISM_ERR_UNSUPPORTED;  // grid size limit
+  if (t->stride_b < 1 || t->stride_s < 1 || t->stride_h < 1) return PRISM_ERR_STRIDE;
+  if (t->head_dim != kHeadDim) return PRISM_ERR_UNSUPPORTED;
+  const int64_t es = esize(t->dtype);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16) return PRISM_ERR_ALIGN;
+  if ((t->stride_b * es) % 16 || (t->stride_s * es) % 16 || (t->stride_h * es) % 16) return PRISM_ERR_ALIGN;
+  return PRISM_OK;
+}
+
+// rows (b, s, h) of an output tensor must not overlap
+bool non_overlapping(const prism_tensor_t *t) {
+  struct D { int64_t stride, extent; } d[3] = {{t->stride_b, t->batch}, {t->stride_s, t->seq}, {t->stride_h, t->heads}};
+  for (int x = 0; x < 3; ++x)
+    for (int y = x + 1; y < 3; ++y)
+      if (d[y].stride < d[x].stride) { D tmp = d[x]; d[x] = d[y]; d[y] = tmp; }
+  int64_t span = t->head_dim;  // elements covered by one row
+  for (int x = 0; x < 3; ++x) {
+    if (d[x].extent == 1) continue;
+    if (d[x].stride < span) return false;
+    span = d[x].stride * d[x].extent;
+  }
+  return true;
+}
+
+int check_qk(const prism_tensor_t *q, const prism_tensor_t *k) {
+  int st = check_tensor(q);
+  if (st) return st;
+  st = check_tensor(k);
+  if (st) return st;
+  if (q->dtype != k->dtype) return PRISM_ERR_DTYPE;
+  if (q->batch != k->batch || q->seq != k->seq || q->head_dim != k->head_dim) return PRISM_ERR_SHAPE;
+  if (q->heads % k->heads) return PRISM_ERR_SHAPE;
+  return PRISM_OK;
+}
+
+int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
+  if (!cfg) return PRISM_ERR_NULL;
+  if (cfg->block_size < 1) return PRISM_ERR_CONFIG;
+  if (cfg->d_high < 2 || cfg->d_high > kHeadDim || cfg->d_high % 2) return PRISM_ERR_CONFIG;
+  if (cfg->d_low < 2 || cfg->d_low > kHeadDim || cfg->d_low % 2) return PRISM_ERR_CONFIG;
+  if (!(cfg->p > 0.0f && cfg->p <= 1.0f)) return PRISM_ERR_CONFIG;
+  if (cfg->causal != 0 && cfg->causal != 1) return PRISM_ERR_CONFIG;
+  if (cfg->rope_layout != PRISM_ROPE_INTERLEAVED && cfg->rope_layout != PRISM_ROPE_HALF) return PRISM_ERR_CONFIG;
+  if (cfg->tau_mode != PRISM_TAU_FULLSPEC && cfg->tau_mode != PRISM_TAU_NONE) return PRISM_ERR_CONFIG;
+  if (cfg->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
+  if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
+  return PRISM_OK;
+}
+
+void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                 prism_workspace_layout_t *L) {
+  const int64_t nb = (q->seq + cfg->block_size - 1) / cfg->block_size;
+  const size_t b = (size_t)q->batch;
+  size_t off = 0;
+  L->qbar_offset = off; off = round_up(off + b * q->heads * nb * kHeadDim * 4, 256);
+  L->kbar_offset = off; off = round_up(off + b * k->heads * nb * kHeadDim * 4, 256);
+  L->qsq_offset = off;  off = round_up(off + b * q->heads * nb * 16, 256);
+  L->ksq_offset = off;  off = round_up(off + b * k->heads * nb * 16, 256);
+  L->tau_offset = off;  off = round_up(off + b * q->heads * 32, 256);
+  L->total_bytes = off;
+  L->nb = nb;
+  const int lo_start = kHeadDim - cfg->d_low;
+  L->seg_lo = cfg->d_high < lo_start ? cfg->d_high : lo_start;
+  L->seg_hi = cfg->d_high < lo_start ? lo_start : cfg->d_high;
+  L->overlap = (cfg->d_high + cfg->d_low > kHeadDim) ? 1 : 0;
+  L->reserved = 0;
+}
+
+prism::TensorArg targ(const prism_tensor_t *t) {
+  prism::TensorArg a;
+  a.data = t->data;
+  a.sb = t->stride_b;
+  a.ss = t->stride_s;
+  a.sh = t->stride_h;
+  a.heads = (int32_t)t->heads;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int prism_abi_version(void) { return PRISM_ABI_VERSION; }
+
+const char *prism_status_str(int status) {
+  switch (status) {
+    case PRISM_OK: return "ok";
+    case PRISM_ERR_NULL: return "null pointer";
+    case PRISM_ERR_DTYPE: return "unsupported or mismatched dtype";
+    case PRISM_ERR_SHAPE: return "inconsistent shape";
+    case PRISM_ERR_STRIDE: return "invalid stride";
+    case PRISM_ERR_ALIGN: return "misaligned pointer or stride";
+    case PRISM_ERR_CONFIG: return "invalid configuration";
+    case PRISM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PRISM_ERR_UNSUPPORTED: return "unsupported size or setting";
+    case PRISM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                                    prism_workspace_layout_t *layout) {
+  int st = check_qk(q, k);
+  if (st) return st;
+  st = check_cfg(cfg, q->seq);
+  if (st) return st;
+  if (!layout) return PRISM_ERR_NULL;
+  make_layout(q, k, cfg, layout);
+  return PRISM_OK;
+}
+
+size_t prism_estimate_workspace_bytes(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg) {
+  prism_workspace_layout_t L;
+  if (prism_estimate_workspace_layout(q, k, cfg, &L) != PRISM_OK) return 0;
+  return L.total_bytes;
+}
+
+int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                   prism_mask_t *mask_out, void *stream) {
+  int st = check_qk(q, k);
+  if (st) return st;
+  st = check_cfg(cfg, q->seq);
+  if (st) return st;
+  prism_workspace_layout_t L;
+  make_layout(q, k, cfg, &L);
+  if (!cfg->workspace || reinterpret_cast<uintptr_t>(cfg->workspace) % 256 || cfg->workspace_bytes < L.total_bytes)
+    return PRISM_ERR_WORKSPACE;
+  if (!mask_out || !mask_out->data) return PRISM_ERR_NULL;
+  if (mask_out->batch != q->batch || mask_out->heads != q->heads || mask_out->nq_blocks != L.nb ||
+      mask_out->nk_blocks != L.nb || mask_out->block_size != cfg->block_size)
+    return PRISM_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(mask_out->data) % 16) return PRISM_ERR_ALIGN;
+
+  char *ws = static_cast<char *>(cfg->workspace);
+  const int fp32 = q->dtype == PRISM_FP32;
+  const int nb = (int)L.nb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  prism::PoolArgs pa;
+  const prism_tensor_t *xs[2] = {q, k};
+  const int per_chunk_max = fp32 ? 8 : 16;  // heads one 256-thread workgroup covers per token
+  for (int t = 0; t < 2; ++t) {
+    pa.x[t] = targ(xs[t]);
+    const int H = (int)xs[t]->heads;
+    const int hc = H < per_chunk_max ? H : per_chunk_max;
+    pa.heads_per_chunk[t] = hc;
+    pa.chunks[t] = (H + hc - 1) / hc;
+  }
+  pa.xbar[0] = reinterpret_cast<float *>(ws + L.qbar_offset);
+  pa.xbar[1] = reinterpret_cast<float *>(ws + L.kbar_offset);
+  pa.sq[0] = reinterpret_cast<float *>(ws + L.qsq_offset);
+  pa.sq[1] = reinterpret_cast<float *>(ws + L.ksq_offset);
+  pa.seq = (int)q->seq;
+  pa.nb = nb;
+  pa.block = cfg->block_size;
+  pa.half_layout = cfg->rope_layout == PRISM_ROPE_HALF;
+  pa.seg_lo = L.seg_lo;
+  pa.seg_hi = L.seg_hi;
+
+  prism::TauArgs ta;
+  ta.qsq = pa.sq[0];
+  ta.ksq = pa.sq[1];
+  ta.tau = reinterpret_cast<float *>(ws + L.tau_offset);
+  ta.hq = (int)q->heads;
+  ta.hkv = (int)k->heads;
+  ta.nb = nb;
+  ta.d_high = cfg->d_high;
+  ta.d_low = cfg->d_low;
+  ta.overlap = L.overlap;
+  ta.tau_none = cfg->tau_mode == PRISM_TAU_NONE;
+
+  prism::SelectArgs sa;
+  sa.qbar = pa.xbar[0];
+  sa.kbar = pa.xbar[1];
+  sa.tau = ta.tau;
+  sa.mask = mask_out->data;
+  sa.hq = ta.hq;
+  sa.hkv = ta.hkv;
+  sa.nb = nb;
+  sa.batch = (int)q->batch;
+  sa.seg_lo = L.seg_lo;
+  sa.seg_hi = L.seg_hi;
+  sa.overlap = L.overlap;
+  sa.d_high = cfg->d_high;
+  sa.d_low = cfg->d_low;
+  sa.causal = cfg->causal;
+  sa.p = cfg->p;
+
+  if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (prism::launch_select(sa, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  return PRISM_OK;
+}
+
+int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, const prism_tensor_t *v,
+                            const prism_mask_t *mask, prism_tensor_t *out, void *stream) {
+  int st = check_qk(q, k);
+  if (st) return st;
+  if ((st = check_tensor(v))) return st;
+  if ((st = check_tensor(out))) return st;
+  if (v->dtype != q->dtype || out->dtype != q->dtype) return PRISM_ERR_DTYPE;
+  if (v->batch != q->batch || v->seq != q->seq || v->heads != k->heads || v->head_dim != q->head_dim)
+    return PRISM_ERR_SHAPE;
+  if (out->batch != q->batch || out->seq != q->seq || out->heads != q->heads || out->head_dim != q->head_dim)
+    return PRISM_ERR_SHAPE;
+  if (!non_overlapping(out)) return PRISM_ERR_STRIDE;
+  if (!mask || !mask->data) return PRISM_ERR_NULL;
+  if (mask->causal != 0 && mask->causal != 1) return PRISM_ERR_CONFIG;
+  if (mask->block_size < 1) return PRISM_ERR_SHAPE;
+  if (mask->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
+  const int64_t nb = (q->seq + kBlock - 1) / kBlock;
+  if (nb > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
+  if (mask->batch != q->batch || mask->heads != q->heads || mask->nq_blocks != nb || mask->nk_blocks != nb)
+    return PRISM_ERR_SHAPE;
+
+  prism::AttnArgs a;
+  a.q = targ(q);
+  a.k = targ(k);
+  a.v = targ(v);
+  a.o = targ(out);
+  a.mask = mask->data;
+  a.batch = (int)q->batch;
+  a.seq = (int)q->seq;
+  a.nb = (int)nb;
+  a.hq = (int)q->heads;
+  a.hkv = (int)k->heads;
+  a.causal = mask->causal;
+  a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = q->dtype == PRISM_BF16 ? prism::launch_attn_bf16(a, s) : prism::launch_attn_fp32(a, s);
+  return e == hipSuccess ? PRISM_OK : PRISM_ERR_LAUNCH;
+}
+
+}  // extern "C"

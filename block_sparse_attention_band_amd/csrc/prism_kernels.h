@@ -1,0 +1,67 @@
+// Internal interface between the C ABI layer (prism_abi.cpp) and the HIP
+// kernels. Arguments reaching these launchers have been validated already.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 128;
+constexpr int kMaxBlocks = 2048;
+
+// One tensor [batch, seq, heads, 128], strides in elements.
+struct TensorArg {
+  const void *data;
+  int64_t sb, ss, sh;
+  int32_t heads;
+};
+
+// ---------------------------------------------------------------- estimator
+struct PoolArgs {
+  TensorArg x[2];        // 0 = Q, 1 = K
+  float *xbar[2];        // [batch][heads][nb][128], canonical frequency order
+  float *sq[2];          // [batch][heads][nb][4]
+  int32_t chunks[2];     // head chunks per tensor
+  int32_t heads_per_chunk[2];
+  int32_t seq, nb, block;
+  int32_t half_layout;   // 1: RoPE pair j = dims (j, j + 64)
+  int32_t seg_lo, seg_hi;
+};
+
+struct TauArgs {
+  const float *qsq, *ksq;  // [batch][H][nb][4]
+  float *tau;              // [batch][Hq][8]
+  int32_t hq, hkv, nb;
+  int32_t d_high, d_low, overlap;
+  int32_t tau_none;
+};
+
+struct SelectArgs {
+  const float *qbar, *kbar, *tau;
+  uint8_t *mask;           // [batch][Hq][nb][nb]
+  int32_t hq, hkv, nb, batch;
+  int32_t seg_lo, seg_hi, overlap;
+  int32_t d_high, d_low;
+  int32_t causal;
+  float p;
+};
+
+hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s);
+hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s);
+hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  TensorArg q, k, v, o;
+  const uint8_t *mask;     // [batch][Hq][nb][nb]
+  int32_t batch, seq, nb, hq, hkv;
+  int32_t causal;
+  float scale_log2;        // log2(e) / sqrt(head_dim)
+};
+
+hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_fp32(const AttnArgs &a, hipStream_t s);
+
+}  // namespace prism

@@ -1,0 +1,392 @@
+// Block-sparse causal attention prefill (Prism abstract; gist.science
+// Technical Summary section 1: attention is computed only on the selected
+// blocks). For query t of query block i, head h (KV head h / G):
+//   out[t] = sum_{s in A(t)} softmax_s(q_t . k_s / sqrt(d)) v_s,
+//   A(t) = { s < N : mask[i][s / 128] == 1, s <= t when causal },
+// and out[t] = 0 when A(t) is empty.
+//
+// bf16 kernel (gfx950 MFMA), one workgroup of 4 waves per (batch, head,
+// query block of 128 tokens); each wave owns 32 query rows.
+//   * The workgroup compacts its mask row into an ascending list of key
+//     blocks in LDS; only those blocks are loaded and computed.
+//   * Keys and values stream in sub-tiles of 64 tokens through two LDS
+//     buffers: the next sub-tile's global loads are in flight while the
+//     current one is computed. V is transposed on its way into LDS.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers. Key
+//     rows are fed to the MFMA in a permuted order chosen so that each lane's
+//     16 accumulator registers per 32-key tile hold, for k-step v, eight
+//     consecutive keys 16v + 8*(lane/32) + 0..7 of one query column. The
+//     softmax'd values are therefore already the B operand (P^T) of
+//     O^T += V^T P^T, and V^T is read with one 16-byte LDS load per MFMA.
+//   * Online softmax in fp32 registers (base 2, scale folded into one FMA);
+//     the causal mask is applied only on the diagonal block, the sequence
+//     end only on the ragged last block.
+//   * Work order: longest rows first; when the KV groups divide evenly over
+//     the 8 XCDs, every XCD owns whole KV groups so a group's K/V tiles are
+//     shared through that XCD's L2.
+// fp32 kernel: same contract in plain fp32 arithmetic (4 threads per query),
+// for fp32 inputs.
+#include "prism_kernels.h"
+
+namespace prism {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kSub = 64;                 // keys per sub-tile
+constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 bytes)
+constexpr int kVStride = kSub + 8;       // bf16 per V^T row in LDS (144 bytes)
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// pack two fp32 to bf16 (round to nearest even) in one dword: lo | hi << 16
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// (batch, head, query block) of this workgroup
+__device__ __forceinline__ void work_item(const AttnArgs &a, int &b, int &h, int &i) {
+  const int bid = blockIdx.x;
+  const int G = a.hq / a.hkv;
+  const int ngroups = a.batch * a.hkv;
+  if (ngroups % kXcds == 0 && (int)gridDim.x % kXcds == 0) {
+    const int xcd = bid % kXcds;
+    const int local = bid / kXcds;
+    const int per_group = G * a.nb;
+    const int slot = local / per_group;
+    const int rem = local % per_group;
+    const int group = xcd + kXcds * slot;
+    b = group / a.hkv;
+    const int g = group % a.hkv;
+    i = a.nb - 1 - rem / G;
+    h = g * G + rem % G;
+  } else {
+    const int nbh = a.batch * a.hq;
+    i = a.nb - 1 - bid / nbh;
+    b = (bid % nbh) / a.hq;
+    h = (bid % nbh) % a.hq;
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kSub * kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim * kVStride];
+  __shared__ int16_t blist[kMaxBlocks];
+  __shared__ int nsel_s;
+
+  int b, h, i;
+  work_item(a, b, h, i);
+  const int g = h / (a.hq / a.hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;  // lane half
+  const int N = a.seq;
+
+  // ---- compact the mask row: selected key blocks in ascending order
+  if (wave == 0) {
+    const uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * a.nb + i) * a.nb;
+    const int jmax = a.causal ? i : a.nb - 1;
+    int cnt = 0;
+    for (int j0 = 0; j0 <= jmax; j0 += 64) {
+      const int j = j0 + lane;
+      const bool sel = j <= jmax && mrow[j] != 0;
+      const uint64_t bal = __ballot(sel);
+      if (sel) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) nsel_s = cnt;
+  }
+
+  // ---- Q rows of this wave as MFMA B operands (registers for the whole loop)
+  const int qrow = i * kBlock + wave * 32 + l32;
+  const bool qvalid = qrow < N;
+  bf16x8 qf[8];
+  {
+    const char *qp = static_cast<const char *>(a.q.data) +
+                     ((int64_t)b * a.q.sb + (int64_t)qrow * a.q.ss + (int64_t)h * a.q.sh) * 2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const uint4 v = qvalid ? ld16(qp + (16 * s + 8 * hf) * 2) : make_uint4(0, 0, 0, 0);
+      qf[s] = as_bf16x8(v);
+    }
+  }
+  __syncthreads();
+  const int nsel = nsel_s;
+  const int nsub = 2 * nsel;
+
+  const char *kbase = static_cast<const char *>(a.k.data) + ((int64_t)b * a.k.sb + (int64_t)g * a.k.sh) * 2;
+  const char *vbase = static_cast<const char *>(a.v.data) + ((int64_t)b * a.v.sb + (int64_t)g * a.v.sh) * 2;
+
+  // global -> register staging of one sub-tile
+  uint4 kreg[4], vreg[4];
+  auto load_sub = [&](int n) {
+    const int kv0 = blist[n >> 1] * kBlock + (n & 1) * kSub;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c >> 4, col = (c & 15) * 8;
+      const int s = kv0 + row;
+      kreg[u] = s < N ? ld16(kbase + ((int64_t)s * a.k.ss + col) * 2) : make_uint4(0, 0, 0, 0);
+    }
+    const int dvo = tid >> 4, kvq = tid & 15;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int s = kv0 + 4 * kvq + x;
+      vreg[x] = s < N ? ld16(vbase + ((int64_t)s * a.v.ss + 8 * dvo) * 2) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_sub = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c >> 4, col = (c & 15) * 8;
+      *reinterpret_cast<uint4 *>(&Ks[buf][row * kKStride + col]) = kreg[u];
+    }
+    // 4 keys x 8 dims -> 8 dims x 4 keys
+    const int dvo = tid >> 4, kvq = tid & 15;
+    const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&vreg[0]);
+    const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&vreg[1]);
+    const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&vreg[2]);
+    const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&vreg[3]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint2 lo, hi;
+      lo.x = (r0[w] & 0xFFFFu) | (r1[w] << 16);
+      lo.y = (r2[w] & 0xFFFFu) | (r3[w] << 16);
+      hi.x = (r0[w] >> 16) | (r1[w] & 0xFFFF0000u);
+      hi.y = (r2[w] >> 16) | (r3[w] & 0xFFFF0000u);
+      *reinterpret_cast<uint2 *>(&Vt[buf][(8 * dvo + 2 * w) * kVStride + 4 * kvq]) = lo;
+      *reinterpret_cast<uint2 *>(&Vt[buf][(8 * dvo + 2 * w + 1) * kVStride + 4 * kvq]) = hi;
+    }
+  };
+
+  // key row fed by this lane to the S^T MFMA (see header comment)
+  const int pm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  if (nsub > 0) {
+    load_sub(0);
+    store_sub(0);
+  }
+  __syncthreads();
+
+  for (int n = 0; n < nsub; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < nsub) load_sub(n + 1);
+
+    const int j = blist[n >> 1];
+    const int kv0 = j * kBlock + (n & 1) * kSub;
+    const bool diag = a.causal && j == i;
+    // whole sub-tile after every query of this wave, or past the sequence end
+    const bool skip = (diag && kv0 > i * kBlock + wave * 32 + 31) || kv0 >= N;
+    if (!skip) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+        const uint16_t *krow = &Ks[buf][(32 * t + pm) * kKStride + 8 * hf];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 16 * s));
+          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+        }
+      }
+      // sacc[t][r] = q_row . k_s with s = kv0 + 32t + 16(r/8) + 8*hf + r%8
+      if (diag || kv0 + kSub > N) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int s = kv0 + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
+            if ((a.causal && s > qrow) || s >= N) sacc[t][r] = -INFINITY;
+          }
+      }
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
+      const float mc = m_use * c;
+      float lsum = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e], c, -mc));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e + 1], c, -mc));
+            lsum += p0 + p1;
+            w[e >> 1] = pack_bf16(p0, p1);
+          }
+          pf[2 * t + v] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+        }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      // O^T[dv][q] += V^T[dv][kv] P^T[kv][q]
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint16_t *vrow = &Vt[buf][(32 * d + l32) * kVStride + 8 * hf];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + 16 * u));
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], oacc[d], 0, 0, 0);
+        }
+      }
+    }
+    if (n + 1 < nsub) store_sub(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: oacc[d][r] = O[qrow][32d + 8(r/4) + 4*hf + r%4]
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if (qvalid) {
+    char *op = static_cast<char *>(const_cast<void *>(a.o.data)) +
+               ((int64_t)b * a.o.sb + (int64_t)qrow * a.o.ss + (int64_t)h * a.o.sh) * 2;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 w;
+        w.x = pack_bf16(oacc[d][4 * r4 + 0] * inv, oacc[d][4 * r4 + 1] * inv);
+        w.y = pack_bf16(oacc[d][4 * r4 + 2] * inv, oacc[d][4 * r4 + 3] * inv);
+        *reinterpret_cast<uint2 *>(op + (32 * d + 8 * r4 + 4 * hf) * 2) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+constexpr int kF32Threads = 512;  // 128 queries x 4 threads
+constexpr int kF32Tile = 32;      // keys per LDS tile
+
+__global__ __launch_bounds__(kF32Threads) void attn_fp32_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float Kt[kF32Tile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * kHeadDim];
+  __shared__ int16_t blist[kMaxBlocks];
+  __shared__ int nsel_s;
+
+  int b, h, i;
+  work_item(a, b, h, i);
+  const int g = h / (a.hq / a.hkv);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int qi = tid >> 2;   // query within the block
+  const int part = tid & 3;  // 32-dim slice
+  const int N = a.seq;
+  const int qrow = i * kBlock + qi;
+  const bool qvalid = qrow < N;
+
+  if (tid < 64) {
+    const uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * a.nb + i) * a.nb;
+    const int jmax = a.causal ? i : a.nb - 1;
+    int cnt = 0;
+    for (int j0 = 0; j0 <= jmax; j0 += 64) {
+      const int j = j0 + lane;
+      const bool sel = j <= jmax && mrow[j] != 0;
+      const uint64_t bal = __ballot(sel);
+      if (sel) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) nsel_s = cnt;
+  }
+
+  float qv[32], ov[32];
+  {
+    const float *qp = static_cast<const float *>(a.q.data) + (int64_t)b * a.q.sb + (int64_t)qrow * a.q.ss +
+                      (int64_t)h * a.q.sh + 32 * part;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) { qv[e] = qvalid ? qp[e] : 0.f; ov[e] = 0.f; }
+  }
+  __syncthreads();
+  const int nsel = nsel_s;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+  const float *kb = static_cast<const float *>(a.k.data) + (int64_t)b * a.k.sb + (int64_t)g * a.k.sh;
+  const float *vb = static_cast<const float *>(a.v.data) + (int64_t)b * a.v.sb + (int64_t)g * a.v.sh;
+
+  for (int n = 0; n < nsel * (kBlock / kF32Tile); ++n) {
+    const int j = blist[n / (kBlock / kF32Tile)];
+    const int kv0 = j * kBlock + (n % (kBlock / kF32Tile)) * kF32Tile;
+    for (int c4 = tid; c4 < kF32Tile * kHeadDim / 4; c4 += kF32Threads) {
+      const int row = c4 / (kHeadDim / 4), col = (c4 % (kHeadDim / 4)) * 4;
+      const int s = kv0 + row;
+      float4 kx = make_float4(0.f, 0.f, 0.f, 0.f), vx = kx;
+      if (s < N) {
+        kx = *reinterpret_cast<const float4 *>(kb + (int64_t)s * a.k.ss + col);
+        vx = *reinterpret_cast<const float4 *>(vb + (int64_t)s * a.v.ss + col);
+      }
+      *reinterpret_cast<float4 *>(&Kt[row * kHeadDim + col]) = kx;
+      *reinterpret_cast<float4 *>(&Vs[row * kHeadDim + col]) = vx;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kF32Tile; ++kk) {
+      const int s = kv0 + kk;
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) dot = fmaf(qv[e], Kt[kk * kHeadDim + 32 * part + e], dot);
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      const bool ok = s < N && (!a.causal || s <= qrow);
+      if (ok) {
+        const float m_new = fmaxf(m_run, dot);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+        const float p = __builtin_amdgcn_exp2f((dot - m_new) * c);
+        l_run = l_run * alpha + p;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) ov[e] = fmaf(p, Vs[kk * kHeadDim + 32 * part + e], ov[e] * alpha);
+        m_run = m_new;
+      }
+    }
+    __syncthreads();
+  }
+  if (qvalid) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    float *op = static_cast<float *>(const_cast<void *>(a.o.data)) + (int64_t)b * a.o.sb + (int64_t)qrow * a.o.ss +
+                (int64_t)h * a.o.sh + 32 * part;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4)
+      *reinterpret_cast<float4 *>(op + e) = make_float4(ov[e] * inv, ov[e + 1] * inv, ov[e + 2] * inv, ov[e + 3] * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(a.batch * a.hq * a.nb), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fp32(const AttnArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_fp32_kernel, dim3(a.batch * a.hq * a.nb), dim3(kF32Threads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace prism

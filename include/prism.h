@@ -1,0 +1,173 @@
+/*
+ * prism.h -- C ABI of libprism: Prism's spectral-aware block-importance
+ * estimator and the causal block-sparse attention prefill that consumes its
+ * block mask, on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Prism: Spectral-Aware Block-Sparse Attention" (arXiv 2602.08426).
+ * The pipeline (Prism review, paper.rainbus.top, pipeline paragraph):
+ *   (1) slice post-RoPE Q, K into a high band (first d_high dims) and a low
+ *       band (last d_low dims); (2) mean-pool each band over blocks of B
+ *       tokens; (3) RMS energy of each pooled band; (4) a per-branch
+ *       temperature tau_z that aligns the branch's logits with the full
+ *       spectrum; (5) S_z = softmax(Qbar_z Kbar_z^T / (tau_z sqrt(d_z)));
+ *       (6) Top-P per branch; (7) M = M_high OR M_low.
+ * Block-sparse prefill (abstract; gist.science Technical Summary section 1)
+ * then computes attention only on the selected (query block, key block) tiles.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer in a descriptor is device memory owned by the caller.
+ *     The library allocates nothing, frees nothing, never synchronises, and
+ *     only enqueues work on `stream` (a hipStream_t; NULL = default stream).
+ *   - Every argument check runs on the host before any HIP call. When a
+ *     check fails the call returns its status, nothing is enqueued and no
+ *     output is touched. PRISM_ERR_LAUNCH reports a failed launch; faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Calls are reentrant and thread-safe; the library keeps no state
+ *     between calls. Two calls that share an output or a workspace and run
+ *     concurrently on different streams race.
+ *   - Tensors are [batch, seq, heads, head_dim] with arbitrary element
+ *     strides for batch, seq and heads (BSHD, BHSD, ...); the head_dim
+ *     stride is 1. Grouped-query attention: query head h reads KV head
+ *     h / (Hq / Hkv); Hq must be a multiple of Hkv.
+ *   - Supported: head_dim 128, block size 128, bf16 throughout or fp32
+ *     throughout, any seq >= 1 (a partial last block is handled), any
+ *     batch >= 1, up to 2048 blocks per sequence (seq <= 262144).
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PRISM_ABI_VERSION 1
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_NULL = 1,        /* a required pointer is NULL */
+  PRISM_ERR_DTYPE = 2,       /* unknown dtype, or the tensors' dtypes differ */
+  PRISM_ERR_SHAPE = 3,       /* sizes inconsistent with each other or non-positive */
+  PRISM_ERR_STRIDE = 4,      /* a stride is non-positive or rows would overlap */
+  PRISM_ERR_ALIGN = 5,       /* data pointer or row start not 16-byte aligned */
+  PRISM_ERR_CONFIG = 6,      /* d_high, d_low, p, rope_layout or tau_mode out of range */
+  PRISM_ERR_WORKSPACE = 7,   /* workspace NULL, not 256-byte aligned, or too small */
+  PRISM_ERR_UNSUPPORTED = 8, /* valid but not built: head_dim != 128, block != 128, too many blocks */
+  PRISM_ERR_LAUNCH = 9       /* a kernel launch failed */
+} prism_status_t;
+
+typedef enum { PRISM_BF16 = 0, PRISM_FP32 = 1 } prism_dtype_t;
+
+/* Where RoPE puts the two coordinates of frequency pair j (frequency falls
+ * with j). INTERLEAVED: dims (2j, 2j+1) -- "first d_high dims" is then the
+ * d_high/2 fastest pairs. HALF (rotate-half): dims (j, j + head_dim/2); the
+ * bands are taken over the same frequency pairs. */
+typedef enum { PRISM_ROPE_INTERLEAVED = 0, PRISM_ROPE_HALF = 1 } prism_rope_layout_t;
+
+/* FULLSPEC: tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full)),
+ *           R = RMS over all pooled blocks of the head and the band's dims;
+ *           tau_z = 1 when any R is 0.
+ * NONE:     tau_z = 1 (plain pooled scores per band). */
+typedef enum { PRISM_TAU_FULLSPEC = 0, PRISM_TAU_NONE = 1 } prism_tau_mode_t;
+
+typedef struct {
+  void *data;        /* device address of element [0, 0, 0, 0] */
+  int32_t dtype;     /* prism_dtype_t */
+  int32_t reserved;  /* set to 0 */
+  int64_t batch, seq, heads, head_dim;
+  int64_t stride_b, stride_s, stride_h; /* in elements; the head_dim stride is 1 */
+} prism_tensor_t;
+
+typedef struct {
+  uint8_t *data;     /* device, row-major [batch][heads][nq_blocks][nk_blocks]; 1 = compute */
+  int64_t batch, heads, nq_blocks, nk_blocks;
+  int32_t block_size;
+  int32_t causal;    /* prism_block_sparse_attn: 1 = blocks above the diagonal are ignored
+                        even when set, and key s is masked for query t when s > t */
+} prism_mask_t;
+
+typedef struct {
+  int32_t block_size; /* B, tokens per block: 128 */
+  int32_t d_high;     /* high-band width, even, 2..head_dim */
+  int32_t d_low;      /* low-band width, even, 2..head_dim */
+  float p;            /* Top-P mass threshold, 0 < p <= 1 (p = 1 keeps every admissible block) */
+  int32_t causal;     /* 1: query block i scores key blocks j <= i only */
+  int32_t rope_layout;/* prism_rope_layout_t */
+  int32_t tau_mode;   /* prism_tau_mode_t */
+  int32_t reserved;   /* set to 0 */
+  void *workspace;    /* device scratch, 256-byte aligned, >= prism_estimate_workspace_bytes() */
+  size_t workspace_bytes;
+} prism_cfg_t;
+
+/* Byte offsets of the estimator's intermediates inside the workspace, valid
+ * after prism_estimate's work has completed on its stream. Pooled vectors are
+ * stored in canonical frequency order: canonical dim 2j and 2j+1 hold RoPE
+ * pair j (for INTERLEAVED this is the physical order). The three segments
+ * [0, seg_lo), [seg_lo, seg_hi), [seg_hi, head_dim) of canonical dims are
+ * high-only, middle and low-only; the middle one belongs to both bands when
+ * `overlap` is 1 (d_high + d_low > head_dim) and to neither when 0. */
+typedef struct {
+  size_t qbar_offset; /* fp32 [batch][Hq][nb][head_dim]: block means of Q */
+  size_t kbar_offset; /* fp32 [batch][Hkv][nb][head_dim]: block means of K */
+  size_t qsq_offset;  /* fp32 [batch][Hq][nb][4]: per-block sums of qbar^2 over the 3 segments, 0 */
+  size_t ksq_offset;  /* fp32 [batch][Hkv][nb][4] */
+  size_t tau_offset;  /* fp32 [batch][Hq][8]: tau_high, tau_low, Rq_high, Rq_low, Rq_full,
+                         Rk_high, Rk_low, Rk_full */
+  size_t total_bytes; /* == prism_estimate_workspace_bytes() */
+  int64_t nb;         /* blocks per sequence, ceil(seq / block_size) */
+  int32_t seg_lo, seg_hi, overlap, reserved;
+} prism_workspace_layout_t;
+
+/* Version of this ABI (PRISM_ABI_VERSION). */
+int prism_abi_version(void);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char *prism_status_str(int status);
+
+/* Workspace bytes prism_estimate needs for these shapes and settings, or 0
+ * when the arguments are invalid (the same checks as prism_estimate, except
+ * the workspace and mask). Host-only; no HIP call. */
+size_t prism_estimate_workspace_bytes(const prism_tensor_t *q, const prism_tensor_t *k,
+                                      const prism_cfg_t *cfg);
+
+/* Fills *layout for these shapes and settings. Host-only; no HIP call.
+ * Returns PRISM_OK or the status prism_estimate would return for the same
+ * q, k and cfg (workspace and mask not checked). */
+int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_t *k,
+                                    const prism_cfg_t *cfg, prism_workspace_layout_t *layout);
+
+/* Prism's block-importance estimator, steps (1)-(7) above.
+ *   q: post-RoPE queries [batch, seq, Hq, head_dim]; k: post-RoPE keys
+ *      [batch, seq, Hkv, head_dim]; same dtype, batch, seq, head_dim.
+ *   cfg: band widths, p, causal flag, RoPE layout, temperature mode, workspace.
+ *   mask_out: written in full, [batch][Hq][nb][nb] uint8 with
+ *      nb = ceil(seq / block_size), block_size == cfg->block_size; every byte
+ *      of the mask is written (0 above the diagonal when causal).
+ * Work: two streaming reads of Q and K (block means and segment energies),
+ * a per-head temperature reduction, and per query block the two band score
+ * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
+ * Deterministic: the same inputs give bit-identical masks and workspace. */
+int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                   prism_mask_t *mask_out, void *stream);
+
+/* Causal block-sparse attention prefill (abstract; gist.science Technical
+ * Summary section 1): for query t of query block i and head h,
+ *   out[t] = sum_{s in A(t)} softmax_s(q_t . k_s / sqrt(head_dim)) v_s,
+ *   A(t) = { s < seq : mask[i][s / B] == 1, and s <= t when mask->causal },
+ * keys and values from KV head h / (Hq / Hkv); out[t] = 0 when A(t) is empty.
+ *   q, out: [batch, seq, Hq, 128]; k, v: [batch, seq, Hkv, 128]; all one dtype.
+ *   mask: [batch][Hq][nb][nb] with block_size 128, e.g. from prism_estimate.
+ * bf16: MFMA products with fp32 accumulation, fp32 online softmax, the
+ * probabilities rounded to bf16 for the P.V product; out rounded to bf16.
+ * fp32: fp32 throughout. Skipped blocks are neither read nor computed.
+ * Deterministic: the same inputs give bit-identical outputs. */
+int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, const prism_tensor_t *v,
+                            const prism_mask_t *mask, prism_tensor_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases compare every element at sizes that span several tiles and a
+ragged tail; the five full-size workloads compare the whole mask and sampled
+query-block rows of the attention output (each row is exact on its own).
+Tolerances: masks per tests/parity.py; bf16 attention max-abs <= 2e-2 and
+norm-relative <= 1e-2; fp32 attention max-abs <= 1e-4 * max|O|.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_attention_band_amd as prism  # noqa: E402
+import oracle.prism_oracle as po  # noqa: E402
+from synth import WORKLOADS, make_qkv, random_mask, to_f64  # noqa: E402
+from tests.parity import compare_masks, oracle_estimate_heads, to_device  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    prism.lib()  # fails loudly when libprism.so is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def cfg_of(w, **kw):
+    c = dict(block_size=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=w.causal)
+    c.update(kw)
+    return prism.EstimatorConfig(**c)
+
+
+def read_ws(ws, off, shape):
+    n = int(np.prod(shape))
+    return ws[off: off + 4 * n].view(torch.float32).reshape(shape).cpu().numpy().astype(np.float64)
+
+
+def canonical(x, rope_layout):
+    """physical dim order -> canonical frequency order (pair j at dims 2j, 2j+1)"""
+    if rope_layout == "interleaved":
+        return x
+    d = x.shape[-1]
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., : d // 2]
+    out[..., 1::2] = x[..., d // 2:]
+    return out
+
+
+# ------------------------------------------------------------ estimator cases
+SMALL = {
+    "gqa4_ragged": ("llama3_8b_32k", dict(seq=3000, hq=8, hkv=2), {}, "bshd", "interleaved"),
+    "planted_qwen": ("qwen3_8b_64k", dict(seq=8192, hq=4, hkv=1), {}, "bshd", "interleaved"),
+    "noncausal": ("llama3_8b_32k", dict(seq=2500, hq=4, hkv=1, causal=False), {}, "bshd", "interleaved"),
+    "gqa8_bhsd": ("llama3_8b_32k", dict(seq=4096, hq=8, hkv=1), {}, "bhsd", "interleaved"),
+    "mha_batch2": ("llama3_8b_32k", dict(seq=2000, hq=2, hkv=2, batch=2), {}, "bshd", "interleaved"),
+    "half_rope": ("llama3_8b_32k", dict(seq=3000, hq=4, hkv=2), {}, "bshd", "half"),
+    "gap_bands": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(d_high=32, d_low=48), "bshd", "interleaved"),
+    "equal_bands": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(d_high=128, d_low=128), "bshd", "interleaved"),
+    "odd_bands": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(d_high=38, d_low=70), "bshd", "interleaved"),
+    "p_half": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(p=0.5), "bshd", "interleaved"),
+    "p_one": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(p=1.0), "bshd", "interleaved"),
+    "tau_none": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(tau_mode="none"), "bshd", "interleaved"),
+    "one_block": ("llama3_8b_32k", dict(seq=100, hq=2, hkv=1), {}, "bshd", "interleaved"),
+    "fp32_iid": ("tiny_fp32_2k", dict(seq=1900, hq=2, hkv=1), {}, "bshd", "interleaved"),
+    "nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128 - 5, hq=1, hkv=1), {}, "bshd", "interleaved"),
+}
+
+
+def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=True):
+    w = WORKLOADS[base].scaled(**over)
+    say(f"[estimator] {name}: seq={w.seq} hq={w.hq} hkv={w.hkv} b={w.batch} {w.dtype} {layout} {cov}")
+    q, k, _ = make_qkv(w, rope_layout=rope_layout, with_v=False)
+    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout})
+    qd, kd = to_device(q, w.dtype, layout), to_device(k, w.dtype, layout)
+    L = prism.workspace_layout(qd, kd, cfg)
+    ws = torch.full((L.total_bytes,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN-poisoned
+    mask = torch.full((w.batch, w.hq, L.nb, L.nb), 7, dtype=torch.uint8, device="cuda")
+    prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+    torch.cuda.synchronize()
+    gm = mask.cpu().numpy()
+    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
+                                causal=cfg.causal, rope_layout=rope_layout, tau_mode=cfg.tau_mode)
+    assert set(np.unique(gm)) <= {0, 1}
+    if cfg.causal:
+        assert not np.triu(gm, 1).any()
+    if check_stages:
+        qbar = read_ws(ws, L.qbar_offset, (w.batch, w.hq, L.nb, 128))
+        kbar = read_ws(ws, L.kbar_offset, (w.batch, w.hkv, L.nb, 128))
+        tau = read_ws(ws, L.tau_offset, (w.batch, w.hq, 8))
+        G = w.hq // w.hkv
+        for (bb, h), r in orc.items():
+            scale = max(1.0, np.abs(r["qbar"]).max())
+            assert np.abs(qbar[bb, h] - canonical(r["qbar"], rope_layout)).max() <= 2e-6 * scale, (bb, h)
+            assert np.abs(kbar[bb, h // G] - canonical(r["kbar"], rope_layout)).max() <= 2e-6 * scale, (bb, h)
+            assert np.allclose(tau[bb, h, :2], r["tau"], rtol=2e-5, atol=0), (tau[bb, h, :2], r["tau"])
+            assert np.allclose(tau[bb, h, 2:5], r["rms_q"], rtol=2e-5, atol=0)
+            assert np.allclose(tau[bb, h, 5:8], r["rms_k"], rtol=2e-5, atol=0)
+    st = compare_masks(gm, orc, cfg.p, cfg.causal)
+    dens = gm.sum() / max(1, st["blocks"])
+    say(f"    density={dens:.4f} blocks={st['blocks']} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
+        f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
+    assert st["unexcused"] == 0, st["where"][:20]
+    return gm, st
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_estimator_small(name):
+    run_estimator_case(name, *SMALL[name])
+
+
+def test_estimator_deterministic_and_overwrites():
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=5000, hq=8, hkv=2)
+    q, k, _ = make_qkv(w, with_v=False)
+    qd, kd = to_device(q, "bf16"), to_device(k, "bf16")
+    cfg = cfg_of(w)
+    outs = []
+    for fill in (0x00, 0xFF):
+        L = prism.workspace_layout(qd, kd, cfg)
+        ws = torch.full((L.total_bytes,), fill, dtype=torch.uint8, device="cuda")
+        m = torch.full((1, w.hq, L.nb, L.nb), fill, dtype=torch.uint8, device="cuda")
+        prism.estimate(qd, kd, cfg, workspace=ws, mask_out=m)
+        torch.cuda.synchronize()
+        outs.append((m.cpu().numpy(), ws[: L.ksq_offset].cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------------------ attention cases
+def oracle_attention(q, k, v, mask, dtype, causal, rows=None):
+    return po.block_sparse_attention(to_f64(q, dtype), to_f64(k, dtype), to_f64(v, dtype), mask, block=128,
+                                     causal=causal, rows=rows)
+
+
+def check_attention(og, oo, dtype, rows_mask=None):
+    og = og.astype(np.float64)
+    if rows_mask is not None:
+        og, oo = og[rows_mask], oo[rows_mask]
+    assert np.isfinite(og).all()
+    err = np.abs(og - oo)
+    if dtype == "bf16":
+        rel = np.linalg.norm(og - oo) / max(np.linalg.norm(oo), 1e-30)
+        say(f"    max_abs={err.max():.3e} rel_norm={rel:.3e} max|O|={np.abs(oo).max():.3e}")
+        assert err.max() <= 2e-2
+        assert rel <= 1e-2
+    else:
+        say(f"    max_abs={err.max():.3e} max|O|={np.abs(oo).max():.3e}")
+        assert err.max() <= 1e-4 * np.abs(oo).max()
+
+
+ATTN = {
+    "dense_causal": ("llama3_8b_32k", dict(seq=1000, hq=4, hkv=2), "ones", True, "bshd"),
+    "random_ragged": ("llama3_8b_32k", dict(seq=2900, hq=4, hkv=1), 0.5, True, "bshd"),
+    "noncausal_random": ("llama3_8b_32k", dict(seq=1500, hq=2, hkv=1), 0.6, False, "bshd"),
+    "noncausal_dense": ("llama3_8b_32k", dict(seq=700, hq=2, hkv=2), "ones", False, "bshd"),
+    "diagonal_only": ("llama3_8b_32k", dict(seq=2000, hq=2, hkv=1), "diag", True, "bshd"),
+    "empty_rows": ("llama3_8b_32k", dict(seq=2048, hq=2, hkv=1), "empty", True, "bshd"),
+    "upper_bits_ignored": ("llama3_8b_32k", dict(seq=1500, hq=2, hkv=1), "full_square", True, "bshd"),
+    "bhsd_gqa8": ("llama3_8b_32k", dict(seq=1800, hq=8, hkv=1), 0.7, True, "bhsd"),
+    "batch2": ("llama3_8b_32k", dict(seq=1300, hq=2, hkv=2, batch=2), 0.5, True, "bshd"),
+    "xcd_groups": ("llama3_8b_32k", dict(seq=1024, hq=16, hkv=8), 0.8, True, "bshd"),
+    "fp32_random": ("tiny_fp32_2k", dict(seq=1500, hq=2, hkv=1), 0.5, True, "bshd"),
+    "fp32_noncausal": ("tiny_fp32_2k", dict(seq=600, hq=1, hkv=1), "ones", False, "bshd"),
+}
+
+
+def make_mask(kind, w, causal, seed=11):
+    nb = w.nb
+    if kind == "ones":
+        m = np.ones((w.batch, w.hq, nb, nb), np.uint8)
+        return m * np.tril(np.ones((nb, nb), np.uint8)) if causal else m
+    if kind == "full_square":
+        return np.ones((w.batch, w.hq, nb, nb), np.uint8)  # upper blocks set but causal
+    if kind == "diag":
+        return np.broadcast_to(np.eye(nb, dtype=np.uint8), (w.batch, w.hq, nb, nb)).copy()
+    if kind == "empty":
+        m = random_mask(w.batch, w.hq, nb, 0.6, seed, causal)
+        m[:, :, 3] = 0
+        m[:, 1, 7] = 0
+        return m
+    return random_mask(w.batch, w.hq, nb, kind, seed, causal)
+
+
+@pytest.mark.parametrize("name", list(ATTN))
+def test_attention_small(name):
+    base, over, kind, causal, layout = ATTN[name]
+    w = WORKLOADS[base].scaled(**over)
+    say(f"[attention] {name}: seq={w.seq} hq={w.hq} hkv={w.hkv} b={w.batch} {w.dtype} mask={kind} causal={causal}")
+    q, k, v = make_qkv(w)
+    mask = make_mask(kind, w, causal)
+    qd, kd, vd = (to_device(x, w.dtype, layout) for x in (q, k, v))
+    md = torch.from_numpy(mask).cuda()
+    out = torch.full_like(qd, float("nan"))
+    prism.block_sparse_attn(qd, kd, vd, md, causal=causal, out=out)
+    torch.cuda.synchronize()
+    og = out.float().cpu().numpy()
+    oo = oracle_attention(q, k, v, mask, w.dtype, causal)
+    check_attention(og, oo, w.dtype)
+    if kind == "empty":
+        assert np.all(og[:, 3 * 128: 4 * 128] == 0)
+
+
+def test_attention_on_estimator_mask_and_deterministic():
+    w = WORKLOADS["qwen3_8b_64k"].scaled(seq=6000, hq=4, hkv=1)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    m = prism.estimate(qd, kd, cfg_of(w))
+    outs = []
+    for _ in range(2):
+        o = torch.full_like(qd, float("nan"))
+        prism.block_sparse_attn(qd, kd, vd, m, out=o)
+        torch.cuda.synchronize()
+        outs.append(o.view(torch.int16).cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    og = torch.from_numpy(outs[0]).view(torch.bfloat16).float().numpy()
+    oo = oracle_attention(q, k, v, m.cpu().numpy(), "bf16", True)
+    check_attention(og, oo, "bf16")
+
+
+# ------------------------------------------------------------ full workloads
+def sample_rows(w, n_rows, seed):
+    rng = np.random.default_rng([seed, 7])
+    nb = w.nb
+    rows = {(0, 0, 0), (0, w.hq - 1, nb - 1)}
+    while len(rows) < n_rows:
+        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.hq)), int(rng.integers(nb))))
+    return sorted(rows)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full(name):
+    w = WORKLOADS[name]
+    say(f"[workload] {name}: generating seq={w.seq} hq={w.hq} hkv={w.hkv} {w.dtype}")
+    q, k, v = make_qkv(w)
+    qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
+    cfg = cfg_of(w)
+    L = prism.workspace_layout(qd, kd, cfg)
+    ws = torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda")
+    mask = torch.full((1, w.hq, L.nb, L.nb), 9, dtype=torch.uint8, device="cuda")
+    prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+    out = torch.full_like(qd, float("nan"))
+    prism.block_sparse_attn(qd, kd, vd, mask, out=out)
+    torch.cuda.synchronize()
+    gm = mask.cpu().numpy()
+    say(f"    GPU done; oracle estimator over {w.hq} heads")
+    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=True)
+    st = compare_masks(gm, orc, w.p, True)
+    say(f"    density={gm.sum() / st['blocks']:.4f} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
+        f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
+    assert st["unexcused"] == 0, st["where"][:20]
+    # attention: sampled query-block rows under the GPU's mask
+    rows = sample_rows(w, 6 if w.seq > 40000 else 12, seed=w.seed)
+    say(f"    oracle attention on rows {rows}")
+    og = out.float().cpu().numpy()
+    assert not np.isnan(og).any()
+    G = w.hq // w.hkv
+    for bb, h, i in rows:
+        t0, t1 = i * 128, min((i + 1) * 128, w.seq)
+        oo = po.attention_block_row(to_f64(q[bb, :, h, :], w.dtype), to_f64(k[bb, :, h // G, :], w.dtype),
+                                    to_f64(v[bb, :, h // G, :], w.dtype), gm[bb, h, i], i, block=128, causal=True)
+        check_attention(og[bb, t0:t1, h, :], oo, w.dtype)
