@@ -1,0 +1,243 @@
+"""Benchmark: Prism estimator + block-sparse causal prefill for one attention
+layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one layer's inputs, resident in
+HBM: prism_estimate (block means and energies, temperatures, scores, Top-P,
+union) followed by prism_block_sparse_attn over the resulting mask. K steps
+are timed back to back between device synchronisations; HIP events around
+each call (on the stream the kernels run on) give the per-phase durations.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "estimator ms + block-sparse prefill ms/layer at 128K; speedup vs dense"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_band_amd", "csrc", "sparse_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_bf16_llama3_8b_128k_traffic.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attention_flops(mask, block, head_dim):
+    """Algorithmic FLOPs of causal block-sparse attention for a uint8 mask
+    [b, H, nb, nb] on the device: 4 B^2 d per selected block below the
+    diagonal, 2 B^2 d per selected diagonal block."""
+    import torch
+    nb = mask.shape[-1]
+    m = mask.bool()
+    diag = torch.diagonal(m, dim1=-2, dim2=-1).sum().item()
+    below = torch.tril(m, diagonal=-1).sum().item()
+    return 4.0 * block * block * head_dim * below + 2.0 * block * block * head_dim * diag, below + diag
+
+
+def traffic_from_profile():
+    """HBM bytes per launch measured by rocprofv3 counters for the current
+    attention kernel source, or None when absent or taken on other source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if vals.get("source_sha256") != sha or "hbm_bytes_per_launch" not in vals:
+        return None
+    return float(vals["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(q, k, v, mask_np, w, budget_s=20.0):
+    """The CPU oracle on a bounded sample of the same layer, extrapolated to
+    ms per layer: the estimator on the query heads of the first KV group(s),
+    the attention on sampled query-block rows of head 0."""
+    import oracle.prism_oracle as po
+    from synth import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    G = w.hq // w.hkv
+    t0 = time.perf_counter()
+    heads_done = 0
+    for g in range(w.hkv):
+        kbar = po.mean_pool(to_f64(k[0, :, g, :], w.dtype), w.block)
+        for h in range(g * G, (g + 1) * G):
+            po.estimate_head(to_f64(q[0, :, h, :], w.dtype), None, block=w.block, d_high=w.d_high, d_low=w.d_low,
+                             p=w.p, causal=True, kbar=kbar)
+            heads_done += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_est = time.perf_counter() - t0
+    est_ms = t_est / heads_done * w.hq * 1e3
+    # attention: rows spread over the causal length, head 0
+    nb = w.nb
+    rows = [nb - 1, (3 * nb) // 4, nb // 2, nb // 4, nb // 8]
+    q0, k0, v0 = to_f64(q[0, :, 0, :], w.dtype), to_f64(k[0, :, 0, :], w.dtype), to_f64(v[0, :, 0, :], w.dtype)
+    t1 = time.perf_counter()
+    blocks_done = 0
+    used = []
+    for i in rows:
+        po.attention_block_row(q0, k0, v0, mask_np[0, 0, i], i, block=w.block, causal=True)
+        blocks_done += int(mask_np[0, 0, i, : i + 1].sum())
+        used.append(i)
+        if time.perf_counter() - t1 > budget_s / 2:
+            break
+    t_attn = time.perf_counter() - t1
+    total_blocks = int(np.tril(mask_np[0]).sum())
+    attn_ms = t_attn / max(1, blocks_done) * total_blocks * 1e3
+    return {
+        "value": round(est_ms + attn_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+        "sample": (f"float64 numpy oracle; estimator on {heads_done} of {w.hq} query heads ({t_est:.1f} s), "
+                   f"attention on query-block rows {used} of head 0 ({blocks_done} selected blocks, {t_attn:.1f} s); "
+                   f"both extrapolated linearly to the whole layer ({w.hq} heads; {total_blocks} selected blocks "
+                   f"over all heads) -- estimator {est_ms:.0f} ms + attention {attn_ms:.0f} ms"),
+        "estimator_ms": round(est_ms, 1), "attention_ms": round(attn_ms, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b_128k")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baselines")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is per head and shards "
+              f"by KV group without any collective -- run one process per GPU on its own heads.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_band_amd as prism
+    from synth import WORKLOADS, make_qkv
+
+    w = WORKLOADS[args.workload]
+    log(f"workload {w.name}: seq={w.seq} hq={w.hq} hkv={w.hkv} {w.dtype}; generating inputs")
+    t = time.perf_counter()
+    q, k, v = make_qkv(w)
+    log(f"inputs ready in {time.perf_counter() - t:.1f}s; uploading")
+
+    def dev(x):
+        if w.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(x).cuda()
+
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    cfg = prism.EstimatorConfig(block_size=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=True)
+    ws = prism.new_workspace(qd, kd, cfg)
+    nb = w.nb
+    mask = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qd)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+        if ev is not None:
+            ev[1].record()
+        prism.block_sparse_attn(qd, kd, vd, mask, out=out)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    est_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"timed: {wall_ms:.3f} ms/step wall, estimator {est_ms:.3f} ms, attention {attn_ms:.3f} ms")
+
+    flops, nsel = attention_flops(mask, w.block, w.head_dim)
+    total_blocks = w.batch * w.hq * nb * (nb + 1) // 2
+    density = nsel / total_blocks
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    elem = 2 if w.dtype == "bf16" else 4
+    est_bytes = (q.size + k.size) * elem + mask.numel()
+    est_gbs = est_bytes / (est_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(wall_ms, 3), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 3), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": w.head_dim, "block": w.block, "d_high": w.d_high, "d_low": w.d_low, "p": w.p,
+                   "rope_theta": w.theta, "causal": True, "parallelism": "none"},
+        "estimator_ms": round(est_ms, 3), "attention_ms": round(attn_ms, 3),
+        "mask_density": round(density, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profile(),
+                     "kernel": "attn_bf16_kernel", "flops_per_launch": flops},
+        "estimator_roofline": {"bound": "hbm", "achieved": round(est_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(est_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": est_bytes},
+    }
+
+    if not args.no_dense:
+        dense = {}
+        ones = torch.tril(torch.ones((nb, nb), dtype=torch.uint8, device="cuda")).expand(w.batch, w.hq, nb, nb).contiguous()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        prism.block_sparse_attn(qd, kd, vd, ones, out=out)
+        e[0].record()
+        for _ in range(2):
+            prism.block_sparse_attn(qd, kd, vd, ones, out=out)
+        e[1].record()
+        torch.cuda.synchronize()
+        dense["own_kernel_all_blocks_ms"] = round(e[0].elapsed_time(e[1]) / 2, 3)
+        try:
+            from torch.nn.attention import SDPBackend, sdpa_kernel
+            G = w.hq // w.hkv
+            qt = qd.permute(0, 2, 1, 3).contiguous()
+            kt = kd.permute(0, 2, 1, 3).repeat_interleave(G, dim=1).contiguous()
+            vt = vd.permute(0, 2, 1, 3).repeat_interleave(G, dim=1).contiguous()
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+                e[0].record()
+                for _ in range(2):
+                    torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+                e[1].record()
+                torch.cuda.synchronize()
+            dense["torch_sdpa_ms"] = round(e[0].elapsed_time(e[1]) / 2, 3)
+            del qt, kt, vt
+        except Exception as ex:  # no fused SDPA backend for this shape / arch
+            dense["torch_sdpa_ms"] = None
+            dense["torch_sdpa_error"] = str(ex)[:160]
+        best = min(x for x in (dense.get("own_kernel_all_blocks_ms"), dense.get("torch_sdpa_ms")) if x)
+        dense["faster"] = "own_kernel" if best == dense["own_kernel_all_blocks_ms"] else "torch_sdpa"
+        result["dense_ms"] = dense
+        result["speedup_vs_dense"] = round(best / (est_ms + attn_ms), 3)
+        log(f"dense: {dense}")
+
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(q, k, v, mask.cpu().numpy(), w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

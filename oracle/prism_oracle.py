@@ -268,14 +268,14 @@ def attention_block_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask_row: n
     logits = (q[t0:t1] @ k[keys].T) / np.sqrt(d)
     if causal:
         logits = np.where(keys[None, :] <= np.arange(t0, t1)[:, None], logits, -np.inf)
-    out = np.zeros((t1 - t0, v.shape[1]))
-    for r in range(t1 - t0):
-        row = logits[r]
-        if not np.isfinite(row).any():
-            continue
-        w = np.exp(row - row.max())
-        out[r] = (w / w.sum()) @ v[keys]
-    return out
+    # row-wise softmax over the admissible keys (exp(-inf) = 0), then the
+    # probability-weighted sum of the values; rows with no admissible key stay 0
+    has = np.isfinite(logits).any(axis=1)
+    rmax = np.where(has, logits.max(axis=1), 0.0)
+    w = np.exp(logits - rmax[:, None])
+    w[~has] = 0.0
+    w[has] /= w[has].sum(axis=1, keepdims=True)
+    return w @ v[keys]
 
 
 def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray, *, block: int,

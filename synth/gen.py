@@ -129,7 +129,7 @@ def _widen(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def _workers() -> int:
-    return max(1, min(8, os.cpu_count() or 1))
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True):
