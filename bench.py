@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_128k")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baselines")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB), the "
+                         "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is per head and shards "
@@ -130,6 +133,15 @@ def main():
     import torch
     import block_sparse_attention_band_amd as prism
     from synth import WORKLOADS, make_qkv
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
 
     w = WORKLOADS[args.workload]
     log(f"workload {w.name}: seq={w.seq} hq={w.hq} hkv={w.hkv} {w.dtype}; generating inputs")

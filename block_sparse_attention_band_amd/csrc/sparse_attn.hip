@@ -18,9 +18,14 @@
 //     consecutive keys 16v + 8*(lane/32) + 0..7 of one query column. The
 //     softmax'd values are therefore already the B operand (P^T) of
 //     O^T += V^T P^T, and V^T is read with one 16-byte LDS load per MFMA.
-//   * Online softmax in fp32 registers (base 2, scale folded into one FMA);
-//     the causal mask is applied only on the diagonal block, the sequence
-//     end only on the ragged last block.
+//   * Online softmax in fp32 registers (base 2, scale folded into one FMA).
+//     The exponent reference only moves, and O and the row sum are only
+//     rescaled, when some query's running max has grown by more than 8 in
+//     log2 units (a wave-wide vote), so most sub-tiles skip the rescale. Row
+//     sums accumulate the bf16-rounded probabilities (the values P.V uses)
+//     with a bf16 dot2. The two lanes sharing a query column combine with a
+//     cross-half lane swap. The causal mask is applied only on the diagonal
+//     block, the sequence end only on the ragged last block.
 //   * Work order: longest rows first; when the KV groups divide evenly over
 //     the 8 XCDs, every XCD owns whole KV groups so a group's K/V tiles are
 //     shared through that XCD's L2.
@@ -46,9 +51,23 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast
 
 // pack two fp32 to bf16 (round to nearest even) in one dword: lo | hi << 16
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr float kLazy = 8.0f;  // log2-domain slack before O and l are rescaled
+
+// max / sum of lane l and lane l^32 (the two lanes holding one query column)
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // (batch, head, query block) of this workgroup
@@ -111,14 +130,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const bool qvalid = qrow < N;
   bf16x8 qf[8];
   {
+    // rows past the sequence end read the last row (never stored)
     const char *qp = static_cast<const char *>(a.q.data) +
-                     ((int64_t)b * a.q.sb + (int64_t)qrow * a.q.ss + (int64_t)h * a.q.sh) * 2;
+                     ((int64_t)b * a.q.sb + (int64_t)min(qrow, N - 1) * a.q.ss + (int64_t)h * a.q.sh) * 2;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint4 v = qvalid ? ld16(qp + (16 * s + 8 * hf) * 2) : make_uint4(0, 0, 0, 0);
-      qf[s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld16(qp + (16 * s + 8 * hf) * 2));
   }
+  // Q must have landed before the loop on every path, so the loop's MFMAs
+  // never wait on the prefetch loads issued inside it: s_waitcnt vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   const int nsel = nsel_s;
   const int nsub = 2 * nsel;
@@ -126,22 +146,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const char *kbase = static_cast<const char *>(a.k.data) + ((int64_t)b * a.k.sb + (int64_t)g * a.k.sh) * 2;
   const char *vbase = static_cast<const char *>(a.v.data) + ((int64_t)b * a.v.sb + (int64_t)g * a.v.sh) * 2;
 
-  // global -> register staging of one sub-tile
+  // global -> register staging of one sub-tile. Byte offsets inside a
+  // sub-tile are fixed per thread; the sub-tile base is wave-uniform.
+  const int64_t kss = a.k.ss * 2, vss = a.v.ss * 2;  // row strides in bytes
+  const int dvo = tid >> 4, kvq = tid & 15;
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = tid + kThreads * u;
+    koff[u] = (uint32_t)((c >> 4) * kss + (c & 15) * 16);
+    voff[u] = (uint32_t)((4 * kvq + u) * vss + dvo * 16);
+  }
   uint4 kreg[4], vreg[4];
   auto load_sub = [&](int n) {
-    const int kv0 = blist[n >> 1] * kBlock + (n & 1) * kSub;
+    const int kv0 = __builtin_amdgcn_readfirstlane((int)blist[n >> 1]) * kBlock + (n & 1) * kSub;
+    const char *kb = kbase + (int64_t)kv0 * kss;
+    const char *vb = vbase + (int64_t)kv0 * vss;
+    if (kv0 + kSub <= N) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c >> 4, col = (c & 15) * 8;
-      const int s = kv0 + row;
-      kreg[u] = s < N ? ld16(kbase + ((int64_t)s * a.k.ss + col) * 2) : make_uint4(0, 0, 0, 0);
-    }
-    const int dvo = tid >> 4, kvq = tid & 15;
+      for (int u = 0; u < 4; ++u) kreg[u] = ld16(kb + koff[u]);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int s = kv0 + 4 * kvq + x;
-      vreg[x] = s < N ? ld16(vbase + ((int64_t)s * a.v.ss + 8 * dvo) * 2) : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) vreg[u] = ld16(vb + voff[u]);
+    } else {
+      // ragged end: rows past the sequence re-read the last row; their
+      // scores are masked and their probabilities are exactly 0
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + kThreads * u;
+        const int64_t r = min(kv0 + (c >> 4), N - 1) - kv0;
+        kreg[u] = ld16(kb + r * kss + (c & 15) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t r = min(kv0 + 4 * kvq + u, N - 1) - kv0;
+        vreg[u] = ld16(vb + r * vss + dvo * 16);
+      }
     }
   };
   auto store_sub = [&](int buf) {
@@ -152,7 +191,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       *reinterpret_cast<uint4 *>(&Ks[buf][row * kKStride + col]) = kreg[u];
     }
     // 4 keys x 8 dims -> 8 dims x 4 keys
-    const int dvo = tid >> 4, kvq = tid & 15;
     const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&vreg[0]);
     const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&vreg[1]);
     const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&vreg[2]);
@@ -177,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   for (int d = 0; d < 4; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[d][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
   if (nsub > 0) {
@@ -222,13 +260,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[t][r]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      const float m_new = fmaxf(m_run, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);
-      const float mc = m_use * c;
-      float lsum = 0.f;
+        for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[t][r], sacc[t][r + 1]));
+      mloc = xhalf_max(mloc);
+      // Lazy rescaling: the exponent reference m_ref only moves (and O, l are
+      // rescaled) when some query's running max exceeds it by more than
+      // kLazy in log2 units; until then p <= 2^kLazy, exact in fp32/bf16 range.
+      const float m_new = fmaxf(m_ref, mloc);
+      if (__any((m_new - m_ref) * c > kLazy)) {
+        const float ref_new = m_new;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - ref_new) * c);
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+        m_ref = ref_new;
+      }
+      const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
       bf16x8 pf[4];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -239,17 +287,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int e = 0; e < 8; e += 2) {
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e], c, -mc));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e + 1], c, -mc));
-            lsum += p0 + p1;
             w[e >> 1] = pack_bf16(p0, p1);
+            // row sum of the rounded probabilities, the values P.V uses
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e >> 1]), kOnes2, l_run, false);
           }
           pf[2 * t + v] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
       // O^T[dv][q] += V^T[dv][kv] P^T[kv][q]
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -266,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- normalise and store: oacc[d][r] = O[qrow][32d + 8(r/4) + 4*hf + r%4]
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   if (qvalid) {
     char *op = static_cast<char *>(const_cast<void *>(a.o.data)) +
