@@ -41,8 +41,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kSub = 64;                 // keys per sub-tile
-constexpr int kKStride = kHeadDim + 8;   // bf16 per K row in LDS (272 bytes)
-constexpr int kVStride = kSub + 8;       // bf16 per V^T row in LDS (144 bytes)
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -94,9 +92,43 @@ __device__ __forceinline__ void work_item(const AttnArgs &a, int &b, int &h, int
   }
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// direct global -> LDS load: each lane's 16 bytes land at lds + 16 * lane
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, LDS_AS uint32_t *lds, int size, int voffset,
+                                                           int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// raw buffer resource over [base, base + nbytes) (wave-uniform)
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ void dma16(const i32x4 &rs, uint8_t *lds, int voff, int soff) {
+  llvm_amdgcn_raw_buffer_load_lds(rs, (LDS_AS uint32_t *)(LDS_AS void *)lds, 16, voff, soff, 0, 0);
+}
+
+// LDS tiles of 64 keys x 128 dims (256-byte rows, 16 chunks of 8 dims).
+// K: chunk c of row r sits in slot c ^ (r & 15): the 16 rows one
+//    ds_read_b128 pass touches land in 16 different bank groups.
+// V: chunk c of row r sits in slot c ^ (4 * (r & 3)): the 4 rows x 4 chunks
+//    a transposing read touches per half-wave land in 16 different groups.
+__device__ __forceinline__ int kslot(int c, int r) { return c ^ (r & 15); }
+__device__ __forceinline__ int vslot(int c, int r) { return c ^ ((r & 3) << 2); }
+
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kSub * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kHeadDim * kVStride];
+  __shared__ __attribute__((aligned(1024))) uint8_t K0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) uint8_t K1[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) uint8_t V0[kSub * 256];
+  __shared__ __attribute__((aligned(1024))) uint8_t V1[kSub * 256];
   __shared__ int16_t blist[kMaxBlocks];
   __shared__ int nsel_s;
 
@@ -105,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int g = h / (a.hq / a.hkv);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
   const int N = a.seq;
@@ -136,79 +168,67 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) qf[s] = as_bf16x8(ld16(qp + (16 * s + 8 * hf) * 2));
   }
-  // Q must have landed before the loop on every path, so the loop's MFMAs
-  // never wait on the prefetch loads issued inside it: s_waitcnt vmcnt(0)
+  // Q must have landed before the loop on every path: s_waitcnt vmcnt(0)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   const int nsel = nsel_s;
   const int nsub = 2 * nsel;
 
+  // ---- K/V of this (batch, KV head) as raw buffers; row strides in bytes
+  const int kss = (int)(a.k.ss * 2), vss = (int)(a.v.ss * 2);
   const char *kbase = static_cast<const char *>(a.k.data) + ((int64_t)b * a.k.sb + (int64_t)g * a.k.sh) * 2;
   const char *vbase = static_cast<const char *>(a.v.data) + ((int64_t)b * a.v.sb + (int64_t)g * a.v.sh) * 2;
+  const i32x4 krs = make_rsrc(kbase, (uint32_t)((N - 1) * kss + 256));
+  const i32x4 vrs = make_rsrc(vbase, (uint32_t)((N - 1) * vss + 256));
 
-  // global -> register staging of one sub-tile. Byte offsets inside a
-  // sub-tile are fixed per thread; the sub-tile base is wave-uniform.
-  const int64_t kss = a.k.ss * 2, vss = a.v.ss * 2;  // row strides in bytes
-  const int dvo = tid >> 4, kvq = tid & 15;
-  uint32_t koff[4], voff[4];
+  // DMA instruction u of wave w fills LDS bytes [(4u + w) * 1024, +1024):
+  // tile rows 4(4u + w) .. +3, lane -> (row + lane/16, slot lane%16)
+  int kdma[4], vdma[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int c = tid + kThreads * u;
-    koff[u] = (uint32_t)((c >> 4) * kss + (c & 15) * 16);
-    voff[u] = (uint32_t)((4 * kvq + u) * vss + dvo * 16);
+    const int row = 4 * (4 * u + wave) + (lane >> 4), slot = lane & 15;
+    kdma[u] = row * kss + (kslot(slot, row) << 4);
+    vdma[u] = row * vss + (vslot(slot, row) << 4);
   }
-  uint4 kreg[4], vreg[4];
-  auto load_sub = [&](int n) {
+  auto dma_sub = [&](int n, uint8_t *Kd, uint8_t *Vd) {
     const int kv0 = __builtin_amdgcn_readfirstlane((int)blist[n >> 1]) * kBlock + (n & 1) * kSub;
-    const char *kb = kbase + (int64_t)kv0 * kss;
-    const char *vb = vbase + (int64_t)kv0 * vss;
     if (kv0 + kSub <= N) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kreg[u] = ld16(kb + koff[u]);
+      for (int u = 0; u < 4; ++u) dma16(krs, Kd + (4 * u + wave) * 1024, kdma[u], kv0 * kss);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vreg[u] = ld16(vb + voff[u]);
+      for (int u = 0; u < 4; ++u) dma16(vrs, Vd + (4 * u + wave) * 1024, vdma[u], kv0 * vss);
     } else {
       // ragged end: rows past the sequence re-read the last row; their
       // scores are masked and their probabilities are exactly 0
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int c = tid + kThreads * u;
-        const int64_t r = min(kv0 + (c >> 4), N - 1) - kv0;
-        kreg[u] = ld16(kb + r * kss + (c & 15) * 16);
+        const int row = 4 * (4 * u + wave) + (lane >> 4), slot = lane & 15;
+        const int r = min(kv0 + row, N - 1);
+        dma16(krs, Kd + (4 * u + wave) * 1024, r * kss + (kslot(slot, row) << 4), 0);
+        dma16(vrs, Vd + (4 * u + wave) * 1024, r * vss + (vslot(slot, row) << 4), 0);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t r = min(kv0 + 4 * kvq + u, N - 1) - kv0;
-        vreg[u] = ld16(vb + r * vss + dvo * 16);
-      }
-    }
-  };
-  auto store_sub = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c >> 4, col = (c & 15) * 8;
-      *reinterpret_cast<uint4 *>(&Ks[buf][row * kKStride + col]) = kreg[u];
-    }
-    // 4 keys x 8 dims -> 8 dims x 4 keys
-    const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&vreg[0]);
-    const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&vreg[1]);
-    const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&vreg[2]);
-    const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&vreg[3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint2 lo, hi;
-      lo.x = (r0[w] & 0xFFFFu) | (r1[w] << 16);
-      lo.y = (r2[w] & 0xFFFFu) | (r3[w] << 16);
-      hi.x = (r0[w] >> 16) | (r1[w] & 0xFFFF0000u);
-      hi.y = (r2[w] >> 16) | (r3[w] & 0xFFFF0000u);
-      *reinterpret_cast<uint2 *>(&Vt[buf][(8 * dvo + 2 * w) * kVStride + 4 * kvq]) = lo;
-      *reinterpret_cast<uint2 *>(&Vt[buf][(8 * dvo + 2 * w + 1) * kVStride + 4 * kvq]) = hi;
     }
   };
 
-  // key row fed by this lane to the S^T MFMA (see header comment)
+  // LDS read offsets. K (A operand of S^T): lane feeds key row 32t + pm,
+  // chunk 2s + hf. V^T (A operand of O^T) by transposing reads: lane group
+  // gr = lane/16 reads rows 16u + 8(gr/2) + (lane%16)/4 (+4 for the upper
+  // half of the k-step) and dims 32d + 16(gr%2) + 4(lane%4); each lane then
+  // holds 4 consecutive keys of dim 32d + lane%32.
   const int pm = 16 * (l32 >> 4) + 8 * ((l32 >> 2) & 1) + 4 * ((l32 >> 3) & 1) + (l32 & 3);
+  int kaddr[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) kaddr[s] = pm * 256 + (kslot(2 * s + hf, pm) << 4);
+  int vaddr[4];
+  {
+    const int gr = (lane >> 4) & 3, s16 = lane & 15;
+    const int row = 8 * (gr >> 1) + (s16 >> 2);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int c = 4 * d + 2 * (gr & 1) + ((s16 & 3) >> 1);
+      vaddr[d] = row * 256 + (vslot(c, row) << 4) + 8 * (s16 & 1);
+    }
+  }
 
   f32x16 oacc[4];
 #pragma unroll
@@ -218,93 +238,99 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float m_ref = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  if (nsub > 0) {
-    load_sub(0);
-    store_sub(0);
-  }
-  __syncthreads();
-
-  for (int n = 0; n < nsub; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < nsub) load_sub(n + 1);
-
-    const int j = blist[n >> 1];
+  auto compute = [&](int n, const uint8_t *Kb, const uint8_t *Vb) {
+    const int j = __builtin_amdgcn_readfirstlane((int)blist[n >> 1]);
     const int kv0 = j * kBlock + (n & 1) * kSub;
     const bool diag = a.causal && j == i;
     // whole sub-tile after every query of this wave, or past the sequence end
-    const bool skip = (diag && kv0 > i * kBlock + wave * 32 + 31) || kv0 >= N;
-    if (!skip) {
-      f32x16 sacc[2];
+    if ((diag && kv0 > i * kBlock + wave * 32 + 31) || kv0 >= N) return;
+    f32x16 sacc[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
-        const uint16_t *krow = &Ks[buf][(32 * t + pm) * kKStride + 8 * hf];
+      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 16 * s));
-          sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
-        }
-      }
-      // sacc[t][r] = q_row . k_s with s = kv0 + 32t + 16(r/8) + 8*hf + r%8
-      if (diag || kv0 + kSub > N) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int s = kv0 + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
-            if ((a.causal && s > qrow) || s >= N) sacc[t][r] = -INFINITY;
-          }
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[t][r], sacc[t][r + 1]));
-      mloc = xhalf_max(mloc);
-      // Lazy rescaling: the exponent reference m_ref only moves (and O, l are
-      // rescaled) when some query's running max exceeds it by more than
-      // kLazy in log2 units; until then p <= 2^kLazy, exact in fp32/bf16 range.
-      const float m_new = fmaxf(m_ref, mloc);
-      if (__any((m_new - m_ref) * c > kLazy)) {
-        const float ref_new = m_new;
-        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - ref_new) * c);
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
-        m_ref = ref_new;
-      }
-      const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
-      bf16x8 pf[4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e], c, -mc));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e + 1], c, -mc));
-            w[e >> 1] = pack_bf16(p0, p1);
-            // row sum of the rounded probabilities, the values P.V uses
-            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e >> 1]), kOnes2, l_run, false);
-          }
-          pf[2 * t + v] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      // O^T[dv][q] += V^T[dv][kv] P^T[kv][q]
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint16_t *vrow = &Vt[buf][(32 * d + l32) * kVStride + 8 * hf];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const bf16x8 vf = as_bf16x8(*reinterpret_cast<const uint4 *>(vrow + 16 * u));
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], oacc[d], 0, 0, 0);
-        }
+      for (int s = 0; s < 8; ++s) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + t * 8192 + kaddr[s]));
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
       }
     }
-    if (n + 1 < nsub) store_sub(buf ^ 1);
+    // sacc[t][r] = q_row . k_s with s = kv0 + 32t + 16(r/8) + 8*hf + r%8
+    if (diag || kv0 + kSub > N) {
+      const int lim = a.causal ? min(qrow, N - 1) : N - 1;  // last admissible key
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int s = kv0 + 32 * t + 16 * (r >> 3) + 8 * hf + (r & 7);
+          sacc[t][r] = s > lim ? -INFINITY : sacc[t][r];
+        }
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[t][r], sacc[t][r + 1]));
+    mloc = xhalf_max(mloc);
+    // Lazy rescaling: the exponent reference m_ref only moves (and O, l are
+    // rescaled) when some query's running max exceeds it by more than
+    // kLazy in log2 units; until then p <= 2^kLazy, exact in fp32/bf16 range.
+    const float m_new = fmaxf(m_ref, mloc);
+    if (__any((m_new - m_ref) * c > kLazy)) {
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_ref - m_new) * c);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[d][r] *= alpha;
+      m_ref = m_new;
+    }
+    const float mc = (m_ref == -INFINITY ? 0.f : m_ref) * c;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e], c, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[t][8 * v + e + 1], c, -mc));
+          w[e >> 1] = pack_bf16(p0, p1);
+          // row sum of the rounded probabilities, the values P.V uses
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e >> 1]), kOnes2, l_run, false);
+        }
+        pf[2 * t + v] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    // O^T[dv][q] += V^T[dv][kv] P^T[kv][q]
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + vaddr[d]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + 1024 + vaddr[d]));
+        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], oacc[d], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsub > 0) {
+    dma_sub(0, K0, V0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+  __syncthreads();
+  for (int n = 0; n < nsub; n += 2) {
+    if (n + 1 < nsub) dma_sub(n + 1, K1, V1);
+    compute(n, K0, V0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (n + 1 >= nsub) break;
+    if (n + 2 < nsub) dma_sub(n + 2, K0, V0);
+    compute(n + 1, K1, V1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
