@@ -4,18 +4,29 @@
 //   S_z[i, :] = softmax over J(i) (j <= i when causal),
 //   M_z[i, :] = Top-P of S_z[i, :] at mass p, and M = M_high OR M_low.
 //
-// One workgroup (8 waves) owns RT consecutive query blocks of one head.
-// Phase 1: the score tile. Both band dot products come from one pass over
-//   the 128 pooled dims split into three segments (high-only, middle,
-//   low-only), on fp32 MFMA 16x16x4 (A = 16 key blocks, B = 16 query
-//   blocks). Logits (already in log2 units) go to LDS as [branch][row][j].
-// Phase 2: selection. One wave per (row, branch): max, exp2, the sum Z, then
-//   the largest threshold T (fp32 bit pattern bisection) with
-//   mass{e >= T} >= p * Z. Entries above T are kept, entries equal to T
-//   are kept in ascending block order until the mass reaches p * Z. This is
-//   the sorted-prefix definition (descending scores, equal scores by lower
-//   index, shortest prefix with mass >= p) without a sort. The union of the
-//   two branches is written as the mask row, zeros included.
+// One workgroup (8 waves) owns RT consecutive query blocks of one head and
+// runs the two branches one after the other (each band is one contiguous
+// range of canonical dims), so one branch's logits fit in ~66 KB of LDS and
+// two workgroups share a CU.
+// Phase 1: the score tile on fp32 MFMA 16x16x4 (A = 16 key blocks, B = 16
+//   query blocks) over the band's dims; 4 waves per SIMD keep key-tile loads
+//   in flight. Logits (in log2 units) go to LDS.
+// Phase 2: selection, one wave per (row, branch), exact and sort-free:
+//   * max, e_j = exp2(L_j - max), and integer masses m_j = e_j * 2^31
+//     (fixed point, so every sum is exact and independent of order);
+//   * a 64-bin histogram of the masses over e's exponent and top two
+//     mantissa bits (quarter octaves, monotone in e) by LDS atomics;
+//   * a wave scan over the bins from the top finds the bin b* where the
+//     cumulative mass first reaches p * Z: bins above b* are kept, bins below
+//     are dropped;
+//   * the (usually few) entries of b* are ranked exactly by (value
+//     descending, block index ascending); an entry is kept when the mass
+//     ranked before it is still short of p * Z.
+//   This is the sorted-prefix definition (shortest prefix of the descending
+//   order with mass >= p, equal scores by lower index) without a sort. A bin
+//   holding more than 64 entries falls back to a bisection over the fp32 bit
+//   pattern of the threshold. The first branch's selection stays in
+//   registers; the union of both is written as the mask row, zeros included.
 #include "prism_kernels.h"
 
 namespace prism {
@@ -124,10 +135,144 @@ __device__ uint32_t select_row(const float (&x)[EPL], float p, int lane) {
   return sel;
 }
 
+// per-wave LDS scratch of the histogram selection
+struct WaveHist {
+  unsigned long long bin[64];  // (count << 52) | fixed-point mass
+  uint32_t cand_key[64];       // the threshold bin's entries: value bits
+  uint32_t cand_j[64];         //   and block index
+};
+
+__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int off) {
+  const int lo = __shfl_up((int)(uint32_t)v, off);
+  const int hi = __shfl_up((int)(uint32_t)(v >> 32), off);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int off) {
+  const int lo = __shfl_xor((int)(uint32_t)v, off);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), off);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// histogram bin of a positive e (bit pattern): quarter octaves from e = 1
+__device__ __forceinline__ int bin_of(uint32_t ebits) { return min(max(508 - (int)(ebits >> 21), 0), 63); }
+
+constexpr float kMassScale = 2147483648.0f;  // fixed point: mass = e * 2^31, e <= 1
+__device__ __forceinline__ uint32_t fixed_mass(uint32_t ebits) {
+  return (uint32_t)(__uint_as_float(ebits) * kMassScale);
+}
+
+// Top-P of one row held by the wave (element k of lane l is block
+// j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits, -inf when j is not
+// admissible; ne4 = number of 4-element slots that hold admissible blocks).
+// Returns this lane's selection bits, or sets *fallback when the threshold
+// bin is too crowded for the exact ranking.
+template <int EPL>
+__device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int lane, WaveHist &H,
+                                    bool *fallback) {
+  *fallback = false;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) mx = fmaxf(mx, x[k]);
+  mx = wave_max(mx);
+  uint32_t valid = 0;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
+  if (p >= 1.0f) return valid;
+
+  H.bin[lane] = 0ull;
+  // key = bit pattern of e (monotone in e); 0 marks an entry that is not
+  // admissible or whose e underflowed to 0 (never needed: p * Z <= Z)
+  uint32_t key[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    key[k] = 0u;
+    if (k / 4 < ne4 && ((valid >> k) & 1u)) {
+      key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
+      if (key[k]) atomicAdd(&H.bin[bin_of(key[k])], (1ull << 52) | fixed_mass(key[k]));
+    }
+  }
+  const unsigned long long hv = H.bin[lane];
+  const unsigned long long mass = hv & ((1ull << 52) - 1ull);
+  const uint32_t cnt = (uint32_t)(hv >> 52);
+  unsigned long long cum = mass;  // inclusive scan over bins, largest values first
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = shfl_up_u64(cum, off);
+    if (lane >= off) cum += y;
+  }
+  const unsigned long long Z = readlane_u64(cum, 63);
+  const unsigned long long target = (unsigned long long)ceil((double)Z * (double)p);
+  const int bstar = __ffsll((long long)__ballot(cum >= target)) - 1;
+  const unsigned long long before = readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
+  const uint32_t c = __builtin_amdgcn_readlane(cnt, bstar);
+
+  uint32_t sel = 0;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k)
+    if (key[k] && bin_of(key[k]) < bstar) sel |= 1u << k;
+  if (c > 64u) {
+    *fallback = true;
+    return 0;
+  }
+  // the threshold bin's entries, ranked by (value desc, index asc)
+  int pos = 0;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    if (k / 4 < ne4) {
+      const bool is = key[k] && bin_of(key[k]) == bstar;
+      const uint64_t bal = __ballot(is);
+      if (is) {
+        const int at = pos + __popcll(bal & ((1ull << lane) - 1ull));
+        H.cand_key[at] = key[k];
+        H.cand_j[at] = 4 * lane + 256 * (k / 4) + (k & 3);
+      }
+      pos += __popcll(bal);
+    }
+  }
+  const uint32_t mk = lane < (int)c ? H.cand_key[lane] : 0u;
+  const uint32_t mj = lane < (int)c ? H.cand_j[lane] : 0u;
+  unsigned long long ahead = 0;  // mass ranked before this entry within the bin
+  for (int q = 0; q < (int)c; q += 4) {
+    uint32_t kk[4], jj[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      kk[u] = q + u < (int)c ? H.cand_key[q + u] : 0u;
+      jj[u] = q + u < (int)c ? H.cand_j[q + u] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (kk[u] > mk || (kk[u] == mk && jj[u] < mj)) ahead += fixed_mass(kk[u]);
+  }
+  const bool chosen = lane < (int)c && before + ahead < target;
+  // the last chosen entry in rank order: smallest value, then largest index
+  unsigned long long cut = chosen ? (((unsigned long long)mk << 11) | (unsigned long long)(2047u - mj)) : ~0ull;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long y = shfl_xor_u64(cut, off);
+    cut = y < cut ? y : cut;
+  }
+  const uint32_t cut_key = (uint32_t)(cut >> 11);
+  const uint32_t cut_j = 2047u - (uint32_t)(cut & 2047ull);
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    if (key[k] && bin_of(key[k]) == bstar) {
+      const uint32_t j = 4 * lane + 256 * (k / 4) + (k & 3);
+      if (key[k] > cut_key || (key[k] == cut_key && j <= cut_j)) sel |= 1u << k;
+    }
+  }
+  return sel;
+}
+
 template <int RT, int EPL>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kThreads, 4) void select_kernel(SelectArgs a) {
   constexpr int NBP = 64 * EPL + 4;  // LDS row length in floats (padded)
-  __shared__ __attribute__((aligned(16))) float lds[2 * RT * NBP];
+  __shared__ __attribute__((aligned(16))) float lds[RT * NBP];  // one branch's logits
+  __shared__ WaveHist whist[kWaves];
 
   const int nb = a.nb;
   const int ntiles = (nb + RT - 1) / RT;
@@ -141,111 +286,131 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   const int i0 = tile * RT;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kq = lane >> 4;   // k slot of the MFMA operands
   const int c16 = lane & 15;  // row of A / column of B
 
   const float *tau = a.tau + ((int64_t)b * a.hq + h) * 8;
   const float kLog2e = 1.4426950408889634f;
-  const float ah = kLog2e / (tau[0] * sqrtf((float)a.d_high));
-  const float al = kLog2e / (tau[1] * sqrtf((float)a.d_low));
-  const float ov = a.overlap ? 1.f : 0.f;
-
-  // ---- phase 1: logits of rows i0..i0+RT-1 against key blocks 0..ncols-1
+  const float *qb = a.qbar + ((int64_t)b * a.hq + h) * nb * kHeadDim;
+  const float *kb = a.kbar + ((int64_t)b * a.hkv + g) * nb * kHeadDim;
   const int ncols = a.causal ? min(nb, i0 + RT) : nb;
-  {
-    const float *qb = a.qbar + ((int64_t)b * a.hq + h) * nb * kHeadDim;
-    const float *kb = a.kbar + ((int64_t)b * a.hkv + g) * nb * kHeadDim;
-    const int iq = i0 + c16;
+  const int nct = (ncols + 15) / 16;
+  const int iq = i0 + c16;
+
+  // selection bits of this wave's rows (r = wave + kWaves * x), per branch
+  constexpr int RPW = (RT + kWaves - 1) / kWaves;
+  uint32_t bits[RPW];
+#pragma unroll
+  for (int x = 0; x < RPW; ++x) bits[x] = 0;
+
+#pragma unroll 1
+  for (int z = 0; z < 2; ++z) {
+    // the branch's band is the canonical dim range [dlo, dhi)
+    const int dlo = z == 0 ? 0 : kHeadDim - a.d_low;
+    const int dhi = z == 0 ? a.d_high : kHeadDim;
+    const float scale = kLog2e / (tau[z] * sqrtf((float)(dhi - dlo)));
+    const int g0 = dlo >> 4, g1 = (dhi + 15) >> 4;  // 16-dim groups the band touches
+
+    // ---- phase 1: logits of rows i0..i0+RT-1 against key blocks 0..ncols-1
     f32x4 qv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      if (iq < nb && c16 < RT) {
+      qv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (q >= g0 && q < g1 && iq < nb && c16 < RT) {
         const float4 t = *reinterpret_cast<const float4 *>(qb + (int64_t)iq * kHeadDim + 16 * q + 4 * kq);
         qv[q] = f32x4{t.x, t.y, t.z, t.w};
-      } else {
-        qv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    const int seg_lo[3] = {0, a.seg_lo, a.seg_hi};
-    const int seg_hi[3] = {a.seg_lo, a.seg_hi, kHeadDim};
-    const int nct = (ncols + 15) / 16;
-    for (int jt = wave; jt < nct; jt += kWaves) {
-      const int j0 = jt * 16;
-      const int jk = j0 + c16;
-      f32x4 kv[8];
+    auto load_k = [&](int jt, f32x4 (&kv)[8]) {
+      const int jk = jt * 16 + c16;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (jk < nb) {
+        kv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (q >= g0 && q < g1 && jk < nb) {
           const float4 t = *reinterpret_cast<const float4 *>(kb + (int64_t)jk * kHeadDim + 16 * q + 4 * kq);
           kv[q] = f32x4{t.x, t.y, t.z, t.w};
-        } else {
-          kv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       }
-      f32x4 acc[3];
-#pragma unroll
-      for (int s = 0; s < 3; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    for (int jt = wave; jt < nct; jt += kWaves) {
+      f32x4 kv[8];
+      load_k(jt, kv);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
+        if (q < g0 || q >= g1) continue;
+        const bool whole = 16 * q >= dlo && 16 * q + 16 <= dhi;
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          const int lo = seg_lo[s], hi = seg_hi[s];
-          if (16 * q >= hi || 16 * q + 16 <= lo) continue;
-          const bool whole = 16 * q >= lo && 16 * q + 16 <= hi;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int dim = 16 * q + 4 * kq + e;
-            const float av = (whole || (dim >= lo && dim < hi)) ? kv[q][e] : 0.f;
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qv[q][e], acc[s], 0, 0, 0);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int dim = 16 * q + 4 * kq + e;
+          const float av = (whole || (dim >= dlo && dim < dhi)) ? kv[q][e] : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qv[q][e], acc, 0, 0, 0);
         }
       }
-      // acc[s][r] = segment-s dot of key block j0 + 4*kq + r with query block i0 + c16
+      // acc[r] = band dot of key block j0 + 4*kq + r with query block i0 + c16
       if (c16 < RT) {
+        const int j0 = jt * 16;
         const int i = i0 + c16;
-        float lh[4], ll[4];
+        float l4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = j0 + 4 * kq + r;
-          const bool ok = j < nb && (!a.causal || j <= i);
-          lh[r] = ok ? (acc[0][r] + ov * acc[1][r]) * ah : -INFINITY;
-          ll[r] = ok ? (acc[2][r] + ov * acc[1][r]) * al : -INFINITY;
+          l4[r] = (j < nb && (!a.causal || j <= i)) ? acc[r] * scale : -INFINITY;
         }
-        *reinterpret_cast<float4 *>(&lds[(0 * RT + c16) * NBP + j0 + 4 * kq]) = make_float4(lh[0], lh[1], lh[2], lh[3]);
-        *reinterpret_cast<float4 *>(&lds[(1 * RT + c16) * NBP + j0 + 4 * kq]) = make_float4(ll[0], ll[1], ll[2], ll[3]);
+        *reinterpret_cast<float4 *>(&lds[c16 * NBP + j0 + 4 * kq]) = make_float4(l4[0], l4[1], l4[2], l4[3]);
       }
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // ---- phase 2: softmax + Top-P per branch, union, mask row
-  for (int r = wave; r < RT; r += kWaves) {
-    const int i = i0 + r;
-    if (i >= nb) continue;
-    const int nc = a.causal ? i + 1 : nb;
-    uint32_t bits = 0;
+    // ---- phase 2: softmax + Top-P of this branch for the wave's rows
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const float *row = &lds[(z * RT + r) * NBP];
-      float x[EPL];
+    for (int x = 0; x < RPW; ++x) {
+      const int r = wave + kWaves * x;
+      const int i = i0 + r;
+      if (r >= RT || i >= nb) continue;
+      const int nc = a.causal ? i + 1 : nb;
+      auto load_row = [&](float (&xr)[EPL]) {
+        const float *row = &lds[r * NBP];
 #pragma unroll
-      for (int e4 = 0; e4 < EPL / 4; ++e4) {
-        const int j = 4 * lane + 256 * e4;
-        float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
-        x[4 * e4 + 0] = t.x;
-        x[4 * e4 + 1] = (j + 1 < nc) ? t.y : -INFINITY;
-        x[4 * e4 + 2] = (j + 2 < nc) ? t.z : -INFINITY;
-        x[4 * e4 + 3] = (j + 3 < nc) ? t.w : -INFINITY;
+        for (int e4 = 0; e4 < EPL / 4; ++e4) {
+          const int j = 4 * lane + 256 * e4;
+          float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+          if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
+          xr[4 * e4 + 0] = t.x;
+          xr[4 * e4 + 1] = (j + 1 < nc) ? t.y : -INFINITY;
+          xr[4 * e4 + 2] = (j + 2 < nc) ? t.z : -INFINITY;
+          xr[4 * e4 + 3] = (j + 3 < nc) ? t.w : -INFINITY;
+        }
+      };
+      bool fallback;
+      uint32_t bz;
+      {
+        float xr[EPL];
+        load_row(xr);
+        bz = select_row_hist<EPL>(xr, (nc + 255) / 256, a.p, lane, whist[wave], &fallback);
       }
-      bits |= select_row<EPL>(x, a.p, lane);
+      if (fallback) {
+        float xr[EPL];
+        load_row(xr);
+        bz = select_row<EPL>(xr, a.p, lane);
+      }
+      bits[x] |= bz;
     }
+    __syncthreads();  // the next branch overwrites the logits
+  }
+
+  // ---- union of the branches -> mask rows, zeros included
+#pragma unroll
+  for (int x = 0; x < RPW; ++x) {
+    const int r = wave + kWaves * x;
+    const int i = i0 + r;
+    if (r >= RT || i >= nb) continue;
     uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * nb + i) * nb;
 #pragma unroll
     for (int e4 = 0; e4 < EPL / 4; ++e4) {
       const int j = 4 * lane + 256 * e4;
-      const uint32_t nib = (bits >> (4 * e4)) & 0xFu;
+      const uint32_t nib = (bits[x] >> (4 * e4)) & 0xFu;
       if ((nb & 3) == 0) {
         if (j < nb) {
           const uint32_t word = (nib & 1u) | ((nib >> 1) & 1u) << 8 | ((nib >> 2) & 1u) << 16 | ((nib >> 3) & 1u) << 24;
