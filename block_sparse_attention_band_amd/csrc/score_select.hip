@@ -169,8 +169,14 @@ __device__ __forceinline__ uint32_t fixed_mass(uint32_t ebits) {
 // Top-P of one row held by the wave (element k of lane l is block
 // j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits, -inf when j is not
 // admissible; ne4 = number of 4-element slots that hold admissible blocks).
-// Returns this lane's selection bits, or sets *fallback when the threshold
-// bin is too crowded for the exact ranking.
+// Radix select on the bit pattern of e = exp2(x - max) (monotone in e):
+// each level histograms the still-undecided entries into 64 bins with exact
+// fixed-point masses, keeps every bin above the one where the cumulative
+// mass reaches p * Z, drops every bin below, and refines that bin (next 6
+// key bits, or the next 64 quarter octaves of the tail) until at most 64
+// entries remain, which are ranked exactly by (value desc, index asc).
+// Returns this lane's selection bits, or sets *fallback if eight levels did
+// not resolve the row.
 template <int EPL>
 __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int lane, WaveHist &H,
                                     bool *fallback) {
@@ -184,71 +190,135 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
   for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
   if (p >= 1.0f) return valid;
 
-  H.bin[lane] = 0ull;
-  // key = bit pattern of e (monotone in e); 0 marks an entry that is not
-  // admissible or whose e underflowed to 0 (never needed: p * Z <= Z)
+  // key = bit pattern of e; 0 marks an entry that is not admissible or whose
+  // e underflowed to 0 (never needed, since p * Z <= Z)
   uint32_t key[EPL];
+  uint32_t act = 0;  // entries still undecided
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
     key[k] = 0u;
-    if (k / 4 < ne4 && ((valid >> k) & 1u)) {
-      key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
-      if (key[k]) atomicAdd(&H.bin[bin_of(key[k])], (1ull << 52) | fixed_mass(key[k]));
+    if (k / 4 < ne4 && ((valid >> k) & 1u)) key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
+    act |= (key[k] ? 1u : 0u) << k;
+  }
+  unsigned long long Z = 0, target = 0, before = 0;
+  uint32_t sel = 0;
+  int shift = 21, base = 508;  // level 0: quarter octaves below e = 1 ...
+  bool tail = true;            // ... with everything smaller in bin 63
+  for (int level = 0; level < 8; ++level) {
+    H.bin[lane] = 0ull;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k)
+      if ((act >> k) & 1u)
+        atomicAdd(&H.bin[min(max(base - (int)(key[k] >> shift), 0), 63)], (1ull << 52) | fixed_mass(key[k]));
+    const unsigned long long hv = H.bin[lane];
+    const unsigned long long mass = hv & ((1ull << 52) - 1ull);
+    unsigned long long cum = mass;  // inclusive scan, largest values first
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const unsigned long long y = shfl_up_u64(cum, off);
+      if (lane >= off) cum += y;
+    }
+    if (level == 0) {
+      Z = readlane_u64(cum, 63);
+      target = (unsigned long long)ceil((double)Z * (double)p);
+    }
+    const unsigned long long need = target - before;  // > 0 at every level
+    const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
+    before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
+    const uint32_t c = (uint32_t)(readlane_u64(hv, bstar) >> 52);
+    uint32_t nact = 0;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      if ((act >> k) & 1u) {
+        const int bk = min(max(base - (int)(key[k] >> shift), 0), 63);
+        if (bk < bstar) sel |= 1u << k;
+        if (bk == bstar) nact |= 1u << k;
+      }
+    }
+    act = nact;
+    if (c <= 64u) break;
+    if (tail && bstar == 63) {
+      base -= 64;  // the next 64 quarter octaves
+      if (base < 63) break;  // only vanishing masses left; ranked below
+    } else if (shift > 0) {
+      const int bits = shift >= 6 ? 6 : shift;
+      shift -= bits;
+      base = ((base - bstar) << bits) + (1 << bits) - 1;
+      tail = false;
+    } else {
+      break;  // all undecided entries share one value; ranked by index below
+    }
+    if (level == 7) {
+      *fallback = true;
+      return 0;
     }
   }
-  const unsigned long long hv = H.bin[lane];
-  const unsigned long long mass = hv & ((1ull << 52) - 1ull);
-  const uint32_t cnt = (uint32_t)(hv >> 52);
-  unsigned long long cum = mass;  // inclusive scan over bins, largest values first
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long y = shfl_up_u64(cum, off);
-    if (lane >= off) cum += y;
-  }
-  const unsigned long long Z = readlane_u64(cum, 63);
-  const unsigned long long target = (unsigned long long)ceil((double)Z * (double)p);
-  const int bstar = __ffsll((long long)__ballot(cum >= target)) - 1;
-  const unsigned long long before = readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
-  const uint32_t c = __builtin_amdgcn_readlane(cnt, bstar);
-
-  uint32_t sel = 0;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k)
-    if (key[k] && bin_of(key[k]) < bstar) sel |= 1u << k;
-  if (c > 64u) {
-    *fallback = true;
-    return 0;
-  }
-  // the threshold bin's entries, ranked by (value desc, index asc)
+  // rank the undecided entries by (value desc, index asc); keep each entry
+  // whose ranked-before mass is still short of the target
   int pos = 0;
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
     if (k / 4 < ne4) {
-      const bool is = key[k] && bin_of(key[k]) == bstar;
+      const bool is = (act >> k) & 1u;
       const uint64_t bal = __ballot(is);
-      if (is) {
-        const int at = pos + __popcll(bal & ((1ull << lane) - 1ull));
+      const int at = pos + __popcll(bal & ((1ull << lane) - 1ull));
+      if (is && at < 64) {
         H.cand_key[at] = key[k];
         H.cand_j[at] = 4 * lane + 256 * (k / 4) + (k & 3);
       }
       pos += __popcll(bal);
     }
   }
-  const uint32_t mk = lane < (int)c ? H.cand_key[lane] : 0u;
-  const uint32_t mj = lane < (int)c ? H.cand_j[lane] : 0u;
-  unsigned long long ahead = 0;  // mass ranked before this entry within the bin
-  for (int q = 0; q < (int)c; q += 4) {
+  if (pos > 64) {
+    // many undecided entries: exact by count when they share one value
+    // (equal masses; index order is (k/4, lane, k%4)), else the fallback
+    uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k)
+      if ((act >> k) & 1u) { kmin = min(kmin, key[k]); kmax = max(kmax, key[k]); }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    if (kmin != kmax) {
+      *fallback = true;
+      return 0;
+    }
+    const unsigned long long m = fixed_mass(kmin);
+    const unsigned long long take = (target - before + m - 1) / m;  // entries needed, >= 1
+    unsigned long long rank0 = 0;
+#pragma unroll
+    for (int e4 = 0; e4 < EPL / 4; ++e4) {
+      const uint32_t nib = (act >> (4 * e4)) & 0xFu;
+      const int cnt = __popc(nib);
+      int r = (int)rank0 + wave_excl_scan_i(cnt, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((nib >> q) & 1u) {
+          if ((unsigned long long)r < take) sel |= 1u << (4 * e4 + q);
+          ++r;
+        }
+      rank0 += (unsigned long long)wave_sum_i(cnt);
+    }
+    return sel;
+  }
+  const int cn = pos;
+  const uint32_t mk = lane < cn ? H.cand_key[lane] : 0u;
+  const uint32_t mj = lane < cn ? H.cand_j[lane] : 0u;
+  unsigned long long ahead = 0;  // mass ranked before this entry
+  for (int q = 0; q < cn; q += 4) {
     uint32_t kk[4], jj[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      kk[u] = q + u < (int)c ? H.cand_key[q + u] : 0u;
-      jj[u] = q + u < (int)c ? H.cand_j[q + u] : 0u;
+      kk[u] = q + u < cn ? H.cand_key[q + u] : 0u;
+      jj[u] = q + u < cn ? H.cand_j[q + u] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (kk[u] > mk || (kk[u] == mk && jj[u] < mj)) ahead += fixed_mass(kk[u]);
   }
-  const bool chosen = lane < (int)c && before + ahead < target;
+  const bool chosen = lane < cn && before + ahead < target;
   // the last chosen entry in rank order: smallest value, then largest index
   unsigned long long cut = chosen ? (((unsigned long long)mk << 11) | (unsigned long long)(2047u - mj)) : ~0ull;
 #pragma unroll
@@ -260,7 +330,7 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
   const uint32_t cut_j = 2047u - (uint32_t)(cut & 2047ull);
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
-    if (key[k] && bin_of(key[k]) == bstar) {
+    if ((act >> k) & 1u) {
       const uint32_t j = 4 * lane + 256 * (k / 4) + (k & 3);
       if (key[k] > cut_key || (key[k] == cut_key && j <= cut_j)) sel |= 1u << k;
     }
@@ -269,7 +339,7 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
 }
 
 template <int RT, int EPL>
-__global__ __launch_bounds__(kThreads, 4) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(kThreads, EPL <= 16 ? 4 : 2) void select_kernel(SelectArgs a) {
   constexpr int NBP = 64 * EPL + 4;  // LDS row length in floats (padded)
   __shared__ __attribute__((aligned(16))) float lds[RT * NBP];  // one branch's logits
   __shared__ WaveHist whist[kWaves];

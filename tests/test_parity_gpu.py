@@ -118,6 +118,50 @@ def test_estimator_small(name):
     run_estimator_case(name, *SMALL[name])
 
 
+def _estimate_and_compare(name, q, k, dtype, cfg):
+    qd, kd = to_device(q, dtype), to_device(k, dtype)
+    mask = prism.estimate(qd, kd, cfg)
+    torch.cuda.synchronize()
+    gm = mask.cpu().numpy()
+    orc = oracle_estimate_heads(q, k, dtype, block=128, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
+                                causal=cfg.causal)
+    st = compare_masks(gm, orc, cfg.p, cfg.causal)
+    say(f"[estimator] {name}: density={gm.sum() / st['blocks']:.4f} mismatch={st['mismatch']} "
+        f"mass_tie={st['mass_tie']} score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
+    assert st["unexcused"] == 0, st["where"][:20]
+    return gm, orc
+
+
+@pytest.mark.parametrize("p", [0.5, 0.95])
+def test_estimator_uniform_rows(p):
+    """Identical blocks: every score of a row ties, so Top-P keeps the
+    ceil(p * n) lowest block indices (more than 64 equal entries per row)."""
+    from synth import f32_to_bf16_bits
+    N = 300 * 128
+    x = f32_to_bf16_bits(np.ones((1, N, 2, 128), np.float32))
+    kx = f32_to_bf16_bits(np.ones((1, N, 1, 128), np.float32))
+    gm, _ = _estimate_and_compare(f"uniform p={p}", x, kx, "bf16", prism.EstimatorConfig(p=p))
+    for i in (0, 1, 99, 299):
+        assert gm[0, 0, i, : i + 1].sum() == int(np.ceil(p * (i + 1) - 1e-12))
+        assert gm[0, 0, i, : int(np.ceil(p * (i + 1) - 1e-12))].all()
+
+
+@pytest.mark.parametrize("a,p", [(1.1, 0.999), (1.3, 0.9999)])
+def test_estimator_peaked_rows_deep_tail(a, p):
+    """One dominant key block and p close to 1: the threshold falls far below
+    the row max (about 2^-12 .. 2^-20 of it, beyond the first 64 quarter
+    octaves for a = 1.3)."""
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(21)
+    N = 200 * 128
+    v = rng.standard_normal(128).astype(np.float32)
+    q = 0.3 * rng.standard_normal((1, N, 2, 128)).astype(np.float32) + a * v
+    k = 0.3 * rng.standard_normal((1, N, 1, 128)).astype(np.float32)
+    k[0, :128, 0, :] += a * v  # key block 0 aligned with every query
+    _estimate_and_compare(f"peaked a={a} p={p}", f32_to_bf16_bits(q), f32_to_bf16_bits(k), "bf16",
+                          prism.EstimatorConfig(p=p))
+
+
 def test_estimator_deterministic_and_overwrites():
     w = WORKLOADS["llama3_8b_32k"].scaled(seq=5000, hq=8, hkv=2)
     q, k, _ = make_qkv(w, with_v=False)
