@@ -89,7 +89,7 @@ def cpu_baseline(q, k, v, mask_np, w, budget_s=20.0):
     est_ms = t_est / heads_done * w.hq * 1e3
     # attention: rows spread over the causal length, head 0
     nb = w.nb
-    rows = [nb - 1, (3 * nb) // 4, nb // 2, nb // 4, nb // 8]
+    rows = sorted({min(nb - 1, max(0, (nb * f) // 16)) for f in range(16, 0, -1)}, reverse=True)
     q0, k0, v0 = to_f64(q[0, :, 0, :], w.dtype), to_f64(k[0, :, 0, :], w.dtype), to_f64(v[0, :, 0, :], w.dtype)
     t1 = time.perf_counter()
     blocks_done = 0

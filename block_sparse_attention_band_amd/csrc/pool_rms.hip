@@ -5,7 +5,8 @@
 // pool_kernel: one streaming pass over Q and K. A workgroup owns one block of
 //   B tokens for a chunk of heads of one tensor; each thread reads 16 bytes
 //   per token (8 bf16 or 4 fp32 dims), so the workgroup's loads for a token
-//   are one contiguous run when heads are adjacent in memory (BSHD). The
+//   are one contiguous run when heads are adjacent in memory (BSHD); the
+//   loads are non-temporal since every byte is read once. The
 //   block sum is accumulated in fp32 in token order, divided by the number
 //   of tokens present, and written in canonical frequency order (dims 2j,
 //   2j+1 = RoPE pair j). The squares of the pooled values are summed per
@@ -46,6 +47,14 @@ struct Elem<true> {  // fp32: 4 dims per 16-byte load
     acc[2] += __uint_as_float(v.z); acc[3] += __uint_as_float(v.w);
   }
 };
+
+// streaming 16-byte load that does not allocate in the caches (Q and K are
+// read exactly once here)
+__device__ __forceinline__ uint4 ld_stream(const char *p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 template <bool FP32>
 __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
@@ -88,11 +97,11 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
     for (; t + 7 * tokp < n; t += 8 * tokp) {
       uint4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4 *>(base + (int64_t)(t + u * tokp) * rs);
+      for (int u = 0; u < 8; ++u) v[u] = ld_stream(base + (int64_t)(t + u * tokp) * rs);
 #pragma unroll
       for (int u = 0; u < 8; ++u) El::add(acc, v[u]);
     }
-    for (; t < n; t += tokp) El::add(acc, *reinterpret_cast<const uint4 *>(base + (int64_t)t * rs));
+    for (; t < n; t += tokp) El::add(acc, ld_stream(base + (int64_t)t * rs));
   }
 
   // combine the token-parallel partial sums in a fixed order
