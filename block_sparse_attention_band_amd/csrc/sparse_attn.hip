@@ -244,17 +244,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const bool diag = a.causal && j == i;
     // whole sub-tile after every query of this wave, or past the sequence end
     if ((diag && kv0 > i * kBlock + wave * 32 + 31) || kv0 >= N) return;
+    // All 16 K fragments of the sub-tile are requested before the first
+    // MFMA, and all 16 V^T fragments right after the last S MFMA (they are in
+    // flight during the softmax): each MFMA then waits for at most one LDS
+    // round trip per sub-tile instead of one per MFMA. The scheduling
+    // barriers keep the compiler from interleaving the reads back into the
+    // MFMA chain.
+    bf16x8 kf[2][8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) kf[t][s] = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + t * 8192 + kaddr[s]));
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4 *>(Kb + t * 8192 + kaddr[s]));
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[t], 0, 0, 0);
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf[s], sacc[t], 0, 0, 0);
+    bf16x8 vf[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + vaddr[d]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + 1024 + vaddr[d]));
+        vf[d][u] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-    }
+    __builtin_amdgcn_sched_barrier(0);
     // sacc[t][r] = q_row . k_s with s = kv0 + 32t + 16(r/8) + 8*hf + r%8
     if (diag || kv0 + kSub > N) {
       const int lim = a.causal ? min(qrow, N - 1) : N - 1;  // last admissible key
@@ -306,14 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + vaddr[d]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (LDS_AS bf16x4 *)(LDS_AS void *)(Vb + u * 4096 + 1024 + vaddr[d]));
-        const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u], oacc[d], 0, 0, 0);
-      }
+      for (int u = 0; u < 4; ++u) oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[d][u], pf[u], oacc[d], 0, 0, 0);
     }
   };
 
