@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 1
+PRISM_ABI_VERSION = 2
 
 # prism_status_t
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH = range(10)
@@ -51,7 +51,8 @@ class PrismCfg(ctypes.Structure):
 class PrismWorkspaceLayout(ctypes.Structure):
     _fields_ = [
         ("qbar_offset", ctypes.c_size_t), ("kbar_offset", ctypes.c_size_t), ("qsq_offset", ctypes.c_size_t),
-        ("ksq_offset", ctypes.c_size_t), ("tau_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+        ("ksq_offset", ctypes.c_size_t), ("tau_offset", ctypes.c_size_t), ("logits_offset", ctypes.c_size_t),
+        ("logits_plane", ctypes.c_int64), ("total_bytes", ctypes.c_size_t),
         ("nb", ctypes.c_int64), ("seg_lo", ctypes.c_int32), ("seg_hi", ctypes.c_int32),
         ("overlap", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]

@@ -81,6 +81,8 @@ void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_c
   L->qsq_offset = off;  off = round_up(off + b * q->heads * nb * 16, 256);
   L->ksq_offset = off;  off = round_up(off + b * k->heads * nb * 16, 256);
   L->tau_offset = off;  off = round_up(off + b * q->heads * 32, 256);
+  L->logits_plane = prism::logit_plane(nb, cfg->causal);
+  L->logits_offset = off; off = round_up(off + b * q->heads * 2 * (size_t)L->logits_plane * 4, 256);
   L->total_bytes = off;
   L->nb = nb;
   const int lo_start = kHeadDim - cfg->d_low;
@@ -193,26 +195,37 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   ta.overlap = L.overlap;
   ta.tau_none = cfg->tau_mode == PRISM_TAU_NONE;
 
-  prism::SelectArgs sa;
-  sa.qbar = pa.xbar[0];
-  sa.kbar = pa.xbar[1];
-  sa.tau = ta.tau;
-  sa.mask = mask_out->data;
-  sa.hq = ta.hq;
-  sa.hkv = ta.hkv;
-  sa.nb = nb;
-  sa.batch = (int)q->batch;
-  sa.seg_lo = L.seg_lo;
-  sa.seg_hi = L.seg_hi;
-  sa.overlap = L.overlap;
-  sa.d_high = cfg->d_high;
-  sa.d_low = cfg->d_low;
-  sa.causal = cfg->causal;
-  sa.p = cfg->p;
+  prism::ScoreArgs sc;
+  sc.qbar = pa.xbar[0];
+  sc.kbar = pa.xbar[1];
+  sc.tau = ta.tau;
+  sc.logits = reinterpret_cast<float *>(ws + L.logits_offset);
+  sc.plane = L.logits_plane;
+  sc.hq = ta.hq;
+  sc.hkv = ta.hkv;
+  sc.nb = nb;
+  sc.batch = (int)q->batch;
+  sc.seg_lo = L.seg_lo;
+  sc.seg_hi = L.seg_hi;
+  sc.overlap = L.overlap;
+  sc.d_high = cfg->d_high;
+  sc.d_low = cfg->d_low;
+  sc.causal = cfg->causal;
+
+  prism::TopPArgs tp;
+  tp.logits = sc.logits;
+  tp.mask = mask_out->data;
+  tp.plane = L.logits_plane;
+  tp.hq = ta.hq;
+  tp.nb = nb;
+  tp.batch = (int)q->batch;
+  tp.causal = cfg->causal;
+  tp.p = cfg->p;
 
   if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
-  if (prism::launch_select(sa, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (prism::launch_score(sc, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (prism::launch_topp(tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   return PRISM_OK;
 }
 

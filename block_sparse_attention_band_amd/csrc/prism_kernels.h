@@ -38,19 +38,42 @@ struct TauArgs {
   int32_t tau_none;
 };
 
-struct SelectArgs {
+// Band logits in the workspace: one fp32 plane per (batch, query head,
+// branch), planes `plane` floats apart. Row i of a plane starts at
+// logit_row(i): packed lower triangle (rows padded to 4 floats) when causal,
+// rows of round_up(nb, 4) floats otherwise.
+__host__ __device__ inline int64_t logit_row(int64_t i, int64_t nb, int causal) {
+  if (!causal) return i * ((nb + 3) & ~int64_t(3));
+  const int64_t q = i >> 2, r = i & 3;  // sum over rows < i of 4 * ceil((row + 1) / 4)
+  return 8 * q * (q + 1) + 4 * r * (q + 1);
+}
+__host__ __device__ inline int64_t logit_plane(int64_t nb, int causal) {
+  return (logit_row(nb, nb, causal) + 63) & ~int64_t(63);  // 256-byte aligned planes
+}
+
+struct ScoreArgs {
   const float *qbar, *kbar, *tau;
-  uint8_t *mask;           // [batch][Hq][nb][nb]
+  float *logits;           // [batch][Hq][2][plane]
+  int64_t plane;
   int32_t hq, hkv, nb, batch;
   int32_t seg_lo, seg_hi, overlap;
   int32_t d_high, d_low;
+  int32_t causal;
+};
+
+struct TopPArgs {
+  const float *logits;
+  uint8_t *mask;           // [batch][Hq][nb][nb]
+  int64_t plane;
+  int32_t hq, nb, batch;
   int32_t causal;
   float p;
 };
 
 hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s);
 hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s);
-hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
+hipError_t launch_topp(const TopPArgs &a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

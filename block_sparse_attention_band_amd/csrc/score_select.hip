@@ -4,14 +4,14 @@
 //   S_z[i, :] = softmax over J(i) (j <= i when causal),
 //   M_z[i, :] = Top-P of S_z[i, :] at mass p, and M = M_high OR M_low.
 //
-// One workgroup (8 waves) owns RT consecutive query blocks of one head and
-// runs the two branches one after the other (each band is one contiguous
-// range of canonical dims), so one branch's logits fit in ~66 KB of LDS and
-// two workgroups share a CU.
-// Phase 1: the score tile on fp32 MFMA 16x16x4 (A = 16 key blocks, B = 16
-//   query blocks) over the band's dims; 4 waves per SIMD keep key-tile loads
-//   in flight. Logits (in log2 units) go to LDS.
-// Phase 2: selection, one wave per (row, branch), exact and sort-free:
+// score_kernel: both branches' logits in one pass. The canonical dims split
+//   into three segments, high-only / middle / low-only; each 64 x 64 tile of
+//   (query block, key block) pairs accumulates the three segment dot products
+//   on fp32 MFMA 32x32x2 (every dim enters once), then
+//   L_high = (s0 + s1) * c_high and L_low = (s1 + s2) * c_low (the middle
+//   segment only when the bands overlap), in log2 units, go to the logit
+//   planes of the workspace.
+// topp_kernel: one wave per (row, both branches); exact and sort-free:
 //   * max, e_j = exp2(L_j - max), and integer masses m_j = e_j * 2^31
 //     (fixed point, so every sum is exact and independent of order);
 //   * a 64-bin histogram of the masses over e's exponent and top two
@@ -24,46 +24,96 @@
 //     ranked before it is still short of p * Z.
 //   This is the sorted-prefix definition (shortest prefix of the descending
 //   order with mass >= p, equal scores by lower index) without a sort. A bin
-//   holding more than 64 entries falls back to a bisection over the fp32 bit
-//   pattern of the threshold. The first branch's selection stays in
-//   registers; the union of both is written as the mask row, zeros included.
+//   holding more than 64 entries is refined on the next key bits; rows that
+//   stay unresolved fall back to a bisection over the fp32 bit pattern of
+//   the threshold. The first branch's selection stays in registers; the
+//   union of both is written as the mask row, zeros included.
 #include "prism_kernels.h"
 
 namespace prism {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+// ---- wave-wide scans and reductions on DPP: Hillis-Steele shifts within
+// each 16-lane row, then the row broadcasts (lane 15 -> rows 1 and 3, lane
+// 31 -> rows 2 and 3). Lane 63 ends with the whole wave's result. No LDS
+// round trips, unlike lane shuffles.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t x) {
+  const uint32_t lo = dpp<CTRL, ROWS>((uint32_t)old, (uint32_t)x);
+  const uint32_t hi = dpp<CTRL, ROWS>((uint32_t)(old >> 32), (uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kBcast15 = 0x142, kBcast31 = 0x143;
+
+// inclusive prefix sum over lanes 0..l (lanes shifted in from outside a
+// row, and rows a broadcast skips, add 0)
+__device__ __forceinline__ uint32_t scan_add(uint32_t x) {
+  x += dpp<kShr1>(0u, x);
+  x += dpp<kShr2>(0u, x);
+  x += dpp<kShr4>(0u, x);
+  x += dpp<kShr8>(0u, x);
+  x += dpp<kBcast15, 0xA>(0u, x);
+  x += dpp<kBcast31, 0xC>(0u, x);
+  return x;
+}
+__device__ __forceinline__ unsigned long long scan_add(unsigned long long x) {
+  x += dpp64<kShr1>(0ull, x);
+  x += dpp64<kShr2>(0ull, x);
+  x += dpp64<kShr4>(0ull, x);
+  x += dpp64<kShr8>(0ull, x);
+  x += dpp64<kBcast15, 0xA>(0ull, x);
+  x += dpp64<kBcast31, 0xC>(0ull, x);
+  return x;
+}
+__device__ __forceinline__ float scan_add(float x) {
+  x += __uint_as_float(dpp<kShr1>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp<kShr2>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp<kShr4>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp<kShr8>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp<kBcast15, 0xA>(0u, __float_as_uint(x)));
+  x += __uint_as_float(dpp<kBcast31, 0xC>(0u, __float_as_uint(x)));
+  return x;
+}
+// running min / max: lanes without a source keep their own value, which
+// min and max leave unchanged, so no identity element is needed
+template <typename Op>
+__device__ __forceinline__ uint32_t scan_keep(uint32_t x, Op op) {
+  x = op(x, dpp<kShr1>(x, x));
+  x = op(x, dpp<kShr2>(x, x));
+  x = op(x, dpp<kShr4>(x, x));
+  x = op(x, dpp<kShr8>(x, x));
+  x = op(x, dpp<kBcast15, 0xA>(x, x));
+  x = op(x, dpp<kBcast31, 0xC>(x, x));
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lane63(uint32_t v) { return __builtin_amdgcn_readlane(v, 63); }
+__device__ __forceinline__ unsigned long long lane63(unsigned long long v) {
+  return ((unsigned long long)__builtin_amdgcn_readlane((uint32_t)(v >> 32), 63) << 32) |
+         __builtin_amdgcn_readlane((uint32_t)v, 63);
+}
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  const uint32_t r = scan_keep(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float(lane63(r));
 }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  return lane63(scan_keep(v, [](uint32_t a, uint32_t b) { return b < a ? b : a; }));
 }
-
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  return lane63(scan_keep(v, [](uint32_t a, uint32_t b) { return b > a ? b : a; }));
 }
-
-__device__ __forceinline__ int wave_excl_scan_i(int v, int lane) {
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x - v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return __uint_as_float(lane63(__float_as_uint(scan_add(v)))); }
+__device__ __forceinline__ int wave_sum_i(int v) { return (int)lane63(scan_add((uint32_t)v)); }
+__device__ __forceinline__ int wave_excl_scan_i(int v, int) { return (int)scan_add((uint32_t)v) - v; }
 
 // Top-P selection of one row held by the wave: element k of lane l is block
 // j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits (-inf when j is not
@@ -138,20 +188,10 @@ __device__ uint32_t select_row(const float (&x)[EPL], float p, int lane) {
 // per-wave LDS scratch of the histogram selection
 struct WaveHist {
   unsigned long long bin[64];  // (count << 52) | fixed-point mass
-  uint32_t cand_key[64];       // the threshold bin's entries: value bits
-  uint32_t cand_j[64];         //   and block index
+  uint32_t cand_key[64];       // the threshold bin's entries (value bits), ascending block order
+  uint32_t cand_keep[64];      // their selection flags
 };
 
-__device__ __forceinline__ unsigned long long shfl_up_u64(unsigned long long v, int off) {
-  const int lo = __shfl_up((int)(uint32_t)v, off);
-  const int hi = __shfl_up((int)(uint32_t)(v >> 32), off);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int off) {
-  const int lo = __shfl_xor((int)(uint32_t)v, off);
-  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), off);
-  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-}
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
@@ -166,347 +206,427 @@ __device__ __forceinline__ uint32_t fixed_mass(uint32_t ebits) {
   return (uint32_t)(__uint_as_float(ebits) * kMassScale);
 }
 
+// The lanes of one wave exchange data through LDS (histogram bins,
+// candidate lists). The hardware runs a wave's LDS instructions in order; this
+// fence keeps the compiler from reordering accesses across the exchange point
+// or forwarding a lane's own earlier store to its later load.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Radix state: the bin of key y is clamp(base - (y >> shift), 0, 63). Level 0
+// bins quarter octaves of e below 1 (base 508 = 4 * 127, shift 21) with every
+// smaller e in bin 63 (tail). Refining bin b* either moves the tail window
+// down so that its bin 0 is the old bin 63's top quarter octave (every bin
+// then holds exactly one value of y >> shift, except the new tail), or splits
+// b* on the next (up to) 6 key bits. Returns false when the keys of b* cannot
+// be split further (all equal) or only masses that round to 0 remain.
+struct Radix {
+  int shift = 21, base = 508;
+  bool tail = true;
+  __device__ int bin(uint32_t y) const { return min(max(base - (int)(y >> shift), 0), 63); }
+  __device__ bool refine(int bstar) {
+    if (tail && bstar == 63) {
+      base -= 63;
+      return base >= 63;
+    }
+    if (shift == 0) return false;
+    const int bits = shift >= 6 ? 6 : shift;
+    shift -= bits;
+    base = ((base - bstar) << bits) + (1 << bits) - 1;
+    tail = false;
+    return true;
+  }
+};
+
+// One histogram pass: entries with `in` set add (1 << 52 | mass) to their
+// bin; returns the threshold bin b* (cumulative mass from the top reaches the
+// target there), adds the mass of the bins above it to `before` and returns
+// b*'s entry count in *count. At the first pass (*Z == 0) it also sets Z and
+// the target ceil(p * Z).
+struct Hist {
+  __device__ static int pass_done(WaveHist &H, int lane, float p, unsigned long long &Z, unsigned long long &target,
+                                  unsigned long long &before, uint32_t *count) {
+    wave_lds_sync();
+    const unsigned long long hv = H.bin[lane];
+    const unsigned long long mass = hv & ((1ull << 52) - 1ull);
+    const unsigned long long cum = scan_add((unsigned long long)mass);  // largest values first
+    if (Z == 0) {
+      Z = readlane_u64(cum, 63);
+      target = (unsigned long long)ceil((double)Z * (double)p);
+    }
+    const unsigned long long need = target - before;  // > 0 at every pass
+    const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
+    before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
+    *count = (uint32_t)(readlane_u64(hv, bstar) >> 52);
+    return bstar;
+  }
+};
+
 // Top-P of one row held by the wave (element k of lane l is block
 // j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits, -inf when j is not
-// admissible; ne4 = number of 4-element slots that hold admissible blocks).
-// Radix select on the bit pattern of e = exp2(x - max) (monotone in e):
-// each level histograms the still-undecided entries into 64 bins with exact
-// fixed-point masses, keeps every bin above the one where the cumulative
-// mass reaches p * Z, drops every bin below, and refines that bin (next 6
-// key bits, or the next 64 quarter octaves of the tail) until at most 64
-// entries remain, which are ranked exactly by (value desc, index asc).
-// Returns this lane's selection bits, or sets *fallback if eight levels did
-// not resolve the row.
+// admissible; slots k/4 >= ne4 hold no admissible block).
+// Radix select on the bit pattern of e = exp2(x - max) (monotone in e) with
+// exact fixed-point masses: each pass histograms the undecided entries into
+// 64 bins, keeps every bin above the one where the cumulative mass reaches
+// p * Z, drops every bin below, and goes on with that bin. Passes run over
+// all entries while the bin holds more than 64 of them; then its entries are
+// compacted in ascending block order (one per lane) and refined there until
+// one entry decides or the rest share one value, which are taken by block
+// index. This is the shortest prefix of the (value desc, index asc) order
+// whose mass reaches p * Z. Returns this lane's selection bits, or sets
+// *fallback when the passes cannot resolve the row.
 template <int EPL>
 __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int lane, WaveHist &H,
                                     bool *fallback) {
   *fallback = false;
   float mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) mx = fmaxf(mx, x[k]);
-  mx = wave_max(mx);
-  uint32_t valid = 0;
+  for (int e4 = 0; e4 < EPL / 4; ++e4) {
+    if (e4 >= ne4) break;
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
-  if (p >= 1.0f) return valid;
+    for (int m = 0; m < 4; ++m) mx = fmaxf(mx, x[4 * e4 + m]);
+  }
+  mx = wave_max(mx);
+  if (p >= 1.0f) {
+    uint32_t valid = 0;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
+    return valid;
+  }
 
-  // key = bit pattern of e; 0 marks an entry that is not admissible or whose
-  // e underflowed to 0 (never needed, since p * Z <= Z)
+  // key = bit pattern of e (exp2(-inf) = 0 marks an entry that is not
+  // admissible; an e that underflows to 0 is never needed since p * Z <= Z)
   uint32_t key[EPL];
   uint32_t act = 0;  // entries still undecided
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    key[k] = 0u;
-    if (k / 4 < ne4 && ((valid >> k) & 1u)) key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
-    act |= (key[k] ? 1u : 0u) << k;
+  for (int k = 0; k < EPL; ++k) key[k] = 0u;
+#pragma unroll
+  for (int e4 = 0; e4 < EPL / 4; ++e4) {
+    if (e4 >= ne4) break;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int k = 4 * e4 + m;
+      key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
+      act |= (key[k] ? 1u : 0u) << k;
+    }
   }
   unsigned long long Z = 0, target = 0, before = 0;
-  uint32_t sel = 0;
-  int shift = 21, base = 508;  // level 0: quarter octaves below e = 1 ...
-  bool tail = true;            // ... with everything smaller in bin 63
-  for (int level = 0; level < 8; ++level) {
+  uint32_t sel = 0, c = 0;
+  Radix R;
+  int bstar = 0;
+  for (int level = 0;; ++level) {
     H.bin[lane] = 0ull;
+    wave_lds_sync();
 #pragma unroll
-    for (int k = 0; k < EPL; ++k)
-      if ((act >> k) & 1u)
-        atomicAdd(&H.bin[min(max(base - (int)(key[k] >> shift), 0), 63)], (1ull << 52) | fixed_mass(key[k]));
-    const unsigned long long hv = H.bin[lane];
-    const unsigned long long mass = hv & ((1ull << 52) - 1ull);
-    unsigned long long cum = mass;  // inclusive scan, largest values first
+    for (int e4 = 0; e4 < EPL / 4; ++e4) {
+      if (e4 >= ne4) break;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const unsigned long long y = shfl_up_u64(cum, off);
-      if (lane >= off) cum += y;
+      for (int m = 0; m < 4; ++m) {
+        const int k = 4 * e4 + m;
+        if ((act >> k) & 1u) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
+      }
     }
-    if (level == 0) {
-      Z = readlane_u64(cum, 63);
-      target = (unsigned long long)ceil((double)Z * (double)p);
-    }
-    const unsigned long long need = target - before;  // > 0 at every level
-    const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
-    before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
-    const uint32_t c = (uint32_t)(readlane_u64(hv, bstar) >> 52);
+    bstar = Hist::pass_done(H, lane, p, Z, target, before, &c);
+    wave_lds_sync();
     uint32_t nact = 0;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      if ((act >> k) & 1u) {
-        const int bk = min(max(base - (int)(key[k] >> shift), 0), 63);
-        if (bk < bstar) sel |= 1u << k;
-        if (bk == bstar) nact |= 1u << k;
+    for (int e4 = 0; e4 < EPL / 4; ++e4) {
+      if (e4 >= ne4) break;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int k = 4 * e4 + m;
+        if ((act >> k) & 1u) {
+          const int bk = R.bin(key[k]);
+          if (bk < bstar) sel |= 1u << k;
+          if (bk == bstar) nact |= 1u << k;
+        }
       }
     }
     act = nact;
     if (c <= 64u) break;
-    if (tail && bstar == 63) {
-      base -= 64;  // the next 64 quarter octaves
-      if (base < 63) break;  // only vanishing masses left; ranked below
-    } else if (shift > 0) {
-      const int bits = shift >= 6 ? 6 : shift;
-      shift -= bits;
-      base = ((base - bstar) << bits) + (1 << bits) - 1;
-      tail = false;
-    } else {
-      break;  // all undecided entries share one value; ranked by index below
+    if (!R.refine(bstar)) {
+      // more than 64 undecided entries of one value: equal masses, taken
+      // by count in ascending block order (k/4, lane, k%4)
+      uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k)
+        if ((act >> k) & 1u) { kmin = min(kmin, key[k]); kmax = max(kmax, key[k]); }
+      kmin = wave_min_u(kmin);
+      kmax = wave_max_u(kmax);
+      const unsigned long long mq = fixed_mass(kmin);
+      if (kmin != kmax || mq == 0) {
+        *fallback = true;
+        return 0;
+      }
+      const unsigned long long take = (target - before + mq - 1) / mq;  // entries needed, >= 1
+      unsigned long long rank0 = 0;
+#pragma unroll
+      for (int e4 = 0; e4 < EPL / 4; ++e4) {
+        const uint32_t nib = (act >> (4 * e4)) & 0xFu;
+        const int cnt = __popc(nib);
+        int r = (int)rank0 + wave_excl_scan_i(cnt, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if ((nib >> q) & 1u) {
+            if ((unsigned long long)r < take) sel |= 1u << (4 * e4 + q);
+            ++r;
+          }
+        rank0 += (unsigned long long)wave_sum_i(cnt);
+      }
+      return sel;
     }
     if (level == 7) {
       *fallback = true;
       return 0;
     }
   }
-  // rank the undecided entries by (value desc, index asc); keep each entry
-  // whose ranked-before mass is still short of the target
-  int pos = 0;
+
+  // compact b*'s entries in ascending block order: slot group e4, then lane,
+  // then k % 4
+  int off[EPL / 4];
+  int total = 0;
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    if (k / 4 < ne4) {
-      const bool is = (act >> k) & 1u;
-      const uint64_t bal = __ballot(is);
-      const int at = pos + __popcll(bal & ((1ull << lane) - 1ull));
-      if (is && at < 64) {
-        H.cand_key[at] = key[k];
-        H.cand_j[at] = 4 * lane + 256 * (k / 4) + (k & 3);
-      }
-      pos += __popcll(bal);
-    }
+  for (int e4 = 0; e4 < EPL / 4; ++e4) {
+    off[e4] = 0;
+    if (e4 >= ne4) continue;
+    const uint32_t nib = (act >> (4 * e4)) & 0xFu;
+    const uint32_t cnt = __popc(nib);
+    const uint32_t incl = scan_add(cnt);
+    off[e4] = total + (int)(incl - cnt);
+    total += (int)lane63(incl);
+    int o = off[e4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if ((nib >> m) & 1u) H.cand_key[o++] = key[4 * e4 + m];
   }
-  if (pos > 64) {
-    // many undecided entries: exact by count when they share one value
-    // (equal masses; index order is (k/4, lane, k%4)), else the fallback
-    uint32_t kmin = ~0u, kmax = 0u;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k)
-      if ((act >> k) & 1u) { kmin = min(kmin, key[k]); kmax = max(kmax, key[k]); }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+
+  // refine on the compacted entries, one per lane
+  wave_lds_sync();
+  const uint32_t ck = lane < (int)c ? H.cand_key[lane] : 0u;
+  bool rem = lane < (int)c;  // still undecided
+  bool keep = false;
+  bool split = R.refine(bstar);
+  for (int level = 0; split && level < 8; ++level) {
+    H.bin[lane] = 0ull;
+    wave_lds_sync();
+    if (rem) atomicAdd(&H.bin[R.bin(ck)], (1ull << 52) | fixed_mass(ck));
+    uint32_t c2;
+    const int b2 = Hist::pass_done(H, lane, p, Z, target, before, &c2);
+    wave_lds_sync();
+    if (rem) {
+      const int bk = R.bin(ck);
+      keep = keep || bk < b2;
+      rem = bk == b2;
     }
-    if (kmin != kmax) {
+    if (c2 == 1u) {  // that entry completes the mass
+      keep = keep || rem;
+      rem = false;
+      break;
+    }
+    split = R.refine(b2);
+  }
+  const uint64_t rb = __ballot(rem);
+  if (rb) {
+    // the undecided entries share one value: the first `take` in list order
+    const uint32_t kv = __builtin_amdgcn_readlane(ck, __ffsll((long long)rb) - 1);
+    const unsigned long long mq = fixed_mass(kv);
+    if (mq == 0) {
       *fallback = true;
       return 0;
     }
-    const unsigned long long m = fixed_mass(kmin);
-    const unsigned long long take = (target - before + m - 1) / m;  // entries needed, >= 1
-    unsigned long long rank0 = 0;
-#pragma unroll
-    for (int e4 = 0; e4 < EPL / 4; ++e4) {
-      const uint32_t nib = (act >> (4 * e4)) & 0xFu;
-      const int cnt = __popc(nib);
-      int r = (int)rank0 + wave_excl_scan_i(cnt, lane);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if ((nib >> q) & 1u) {
-          if ((unsigned long long)r < take) sel |= 1u << (4 * e4 + q);
-          ++r;
-        }
-      rank0 += (unsigned long long)wave_sum_i(cnt);
-    }
-    return sel;
+    const unsigned long long take = (target - before + mq - 1) / mq;
+    const unsigned long long r = __popcll(rb & ((1ull << lane) - 1ull));
+    keep = keep || (rem && r < take);
   }
-  const int cn = pos;
-  const uint32_t mk = lane < cn ? H.cand_key[lane] : 0u;
-  const uint32_t mj = lane < cn ? H.cand_j[lane] : 0u;
-  unsigned long long ahead = 0;  // mass ranked before this entry
-  for (int q = 0; q < cn; q += 4) {
-    uint32_t kk[4], jj[4];
+  H.cand_keep[lane] = keep ? 1u : 0u;
+  wave_lds_sync();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      kk[u] = q + u < cn ? H.cand_key[q + u] : 0u;
-      jj[u] = q + u < cn ? H.cand_j[q + u] : 0u;
-    }
+  for (int e4 = 0; e4 < EPL / 4; ++e4) {
+    if (e4 >= ne4) continue;
+    const uint32_t nib = (act >> (4 * e4)) & 0xFu;
+    int o = off[e4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (kk[u] > mk || (kk[u] == mk && jj[u] < mj)) ahead += fixed_mass(kk[u]);
-  }
-  const bool chosen = lane < cn && before + ahead < target;
-  // the last chosen entry in rank order: smallest value, then largest index
-  unsigned long long cut = chosen ? (((unsigned long long)mk << 11) | (unsigned long long)(2047u - mj)) : ~0ull;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const unsigned long long y = shfl_xor_u64(cut, off);
-    cut = y < cut ? y : cut;
-  }
-  const uint32_t cut_key = (uint32_t)(cut >> 11);
-  const uint32_t cut_j = 2047u - (uint32_t)(cut & 2047ull);
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    if ((act >> k) & 1u) {
-      const uint32_t j = 4 * lane + 256 * (k / 4) + (k & 3);
-      if (key[k] > cut_key || (key[k] == cut_key && j <= cut_j)) sel |= 1u << k;
-    }
+    for (int m = 0; m < 4; ++m)
+      if ((nib >> m) & 1u) {
+        if (H.cand_keep[o]) sel |= 1u << (4 * e4 + m);
+        ++o;
+      }
   }
   return sel;
 }
 
-template <int RT, int EPL>
-__global__ __launch_bounds__(kThreads, EPL <= 16 ? 4 : 2) void select_kernel(SelectArgs a) {
-  constexpr int NBP = 64 * EPL + 4;  // LDS row length in floats (padded)
-  __shared__ __attribute__((aligned(16))) float lds[RT * NBP];  // one branch's logits
-  __shared__ WaveHist whist[kWaves];
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-  const int nb = a.nb;
-  const int ntiles = (nb + RT - 1) / RT;
-  const int nbh = a.hq * a.batch;
-  const int bid = blockIdx.x;
-  const int tile = a.causal ? (ntiles - 1 - bid / nbh) : (bid / nbh);  // longest rows first
-  const int bh = bid % nbh;
-  const int b = bh / a.hq;
-  const int h = bh % a.hq;
-  const int g = h / (a.hq / a.hkv);
-  const int i0 = tile * RT;
+// segment of canonical dim d: 0 high-only, 1 middle, 2 low-only
+__device__ __forceinline__ int seg_of(int d, int lo, int hi) { return d < lo ? 0 : (d < hi ? 1 : 2); }
 
+// One workgroup = one 64 x 64 tile (query blocks I*64.., key blocks J*64..)
+// of one head; wave w owns the 32 x 32 quadrant (w / 2, w % 2). MFMA operands:
+// lane l gives query row l % 32 and key row l % 32 of its quadrant, and the
+// dims 8c + 4(l / 32) + e for the MFMA e of chunk c; A and B use the same
+// dim for the same k, so each chunk's 8 dims are summed exactly once.
+__global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
+  const int nI = (a.nb + 63) / 64;
+  const int tiles = a.causal ? nI * (nI + 1) / 2 : nI * nI;
+  const int bh = blockIdx.x / tiles;
+  const int t = blockIdx.x % tiles;
+  int I, J;
+  if (a.causal) {
+    I = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((I + 1) * (I + 2) / 2 <= t) ++I;
+    while (I * (I + 1) / 2 > t) --I;
+    J = t - I * (I + 1) / 2;
+  } else {
+    I = t / nI;
+    J = t % nI;
+  }
+  const int b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kq = lane >> 4;   // k slot of the MFMA operands
-  const int c16 = lane & 15;  // row of A / column of B
+  const int r32 = lane & 31, hf = lane >> 5;
+  const int i0 = I * 64 + 32 * (wave >> 1), j0 = J * 64 + 32 * (wave & 1);
+  if (i0 >= a.nb || j0 >= a.nb) return;
+  if (a.causal && j0 > i0 + 31) return;  // quadrant entirely above the diagonal
 
-  const float *tau = a.tau + ((int64_t)b * a.hq + h) * 8;
-  const float kLog2e = 1.4426950408889634f;
-  const float *qb = a.qbar + ((int64_t)b * a.hq + h) * nb * kHeadDim;
-  const float *kb = a.kbar + ((int64_t)b * a.hkv + g) * nb * kHeadDim;
-  const int ncols = a.causal ? min(nb, i0 + RT) : nb;
-  const int nct = (ncols + 15) / 16;
-  const int iq = i0 + c16;
-
-  // selection bits of this wave's rows (r = wave + kWaves * x), per branch
-  constexpr int RPW = (RT + kWaves - 1) / kWaves;
-  uint32_t bits[RPW];
+  const float *qp = a.qbar + ((int64_t)bh * a.nb + min(i0 + r32, a.nb - 1)) * kHeadDim + 4 * hf;
+  const float *kp = a.kbar + (((int64_t)b * a.hkv + g) * a.nb + min(j0 + r32, a.nb - 1)) * kHeadDim + 4 * hf;
+  float4 qa[16], ka[16];
 #pragma unroll
-  for (int x = 0; x < RPW; ++x) bits[x] = 0;
-
-#pragma unroll 1
-  for (int z = 0; z < 2; ++z) {
-    // the branch's band is the canonical dim range [dlo, dhi)
-    const int dlo = z == 0 ? 0 : kHeadDim - a.d_low;
-    const int dhi = z == 0 ? a.d_high : kHeadDim;
-    const float scale = kLog2e / (tau[z] * sqrtf((float)(dhi - dlo)));
-    const int g0 = dlo >> 4, g1 = (dhi + 15) >> 4;  // 16-dim groups the band touches
-
-    // ---- phase 1: logits of rows i0..i0+RT-1 against key blocks 0..ncols-1
-    f32x4 qv[8];
+  for (int c = 0; c < 16; ++c) {
+    qa[c] = *reinterpret_cast<const float4 *>(qp + 8 * c);
+    ka[c] = *reinterpret_cast<const float4 *>(kp + 8 * c);
+  }
+  f32x16 acc0, acc1, acc2;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      qv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (q >= g0 && q < g1 && iq < nb && c16 < RT) {
-        const float4 t = *reinterpret_cast<const float4 *>(qb + (int64_t)iq * kHeadDim + 16 * q + 4 * kq);
-        qv[q] = f32x4{t.x, t.y, t.z, t.w};
-      }
+  for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; acc2[r] = 0.f; }
+  const int lo = a.seg_lo, hi = a.seg_hi;
+  // Each accumulator has its own (wave-uniform) branch per chunk, so no
+  // accumulator is ever selected at run time. A chunk inside one segment
+  // feeds that segment only; a chunk across a boundary feeds each segment it
+  // touches with the other segments' dims zeroed.
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const float qv[4] = {qa[c].x, qa[c].y, qa[c].z, qa[c].w};
+    const float kv[4] = {ka[c].x, ka[c].y, ka[c].z, ka[c].w};
+    const bool t0 = 8 * c < lo;
+    const bool t1 = a.overlap && 8 * c + 7 >= lo && 8 * c < hi;
+    const bool t2 = 8 * c + 7 >= hi;
+    const bool whole = seg_of(8 * c, lo, hi) == seg_of(8 * c + 7, lo, hi);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int sd = seg_of(8 * c + 4 * hf + e, lo, hi);
+      if (t0) acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 0) ? qv[e] : 0.f, kv[e], acc0, 0, 0, 0);
+      if (t1) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 1) ? qv[e] : 0.f, kv[e], acc1, 0, 0, 0);
+      if (t2) acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 2) ? qv[e] : 0.f, kv[e], acc2, 0, 0, 0);
     }
-    auto load_k = [&](int jt, f32x4 (&kv)[8]) {
-      const int jk = jt * 16 + c16;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        kv[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (q >= g0 && q < g1 && jk < nb) {
-          const float4 t = *reinterpret_cast<const float4 *>(kb + (int64_t)jk * kHeadDim + 16 * q + 4 * kq);
-          kv[q] = f32x4{t.x, t.y, t.z, t.w};
-        }
-      }
-    };
-    for (int jt = wave; jt < nct; jt += kWaves) {
-      f32x4 kv[8];
-      load_k(jt, kv);
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q < g0 || q >= g1) continue;
-        const bool whole = 16 * q >= dlo && 16 * q + 16 <= dhi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int dim = 16 * q + 4 * kq + e;
-          const float av = (whole || (dim >= dlo && dim < dhi)) ? kv[q][e] : 0.f;
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, qv[q][e], acc, 0, 0, 0);
-        }
-      }
-      // acc[r] = band dot of key block j0 + 4*kq + r with query block i0 + c16
-      if (c16 < RT) {
-        const int j0 = jt * 16;
-        const int i = i0 + c16;
-        float l4[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = j0 + 4 * kq + r;
-          l4[r] = (j < nb && (!a.causal || j <= i)) ? acc[r] * scale : -INFINITY;
-        }
-        *reinterpret_cast<float4 *>(&lds[c16 * NBP + j0 + 4 * kq]) = make_float4(l4[0], l4[1], l4[2], l4[3]);
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 2: softmax + Top-P of this branch for the wave's rows
-#pragma unroll
-    for (int x = 0; x < RPW; ++x) {
-      const int r = wave + kWaves * x;
-      const int i = i0 + r;
-      if (r >= RT || i >= nb) continue;
-      const int nc = a.causal ? i + 1 : nb;
-      auto load_row = [&](float (&xr)[EPL]) {
-        const float *row = &lds[r * NBP];
-#pragma unroll
-        for (int e4 = 0; e4 < EPL / 4; ++e4) {
-          const int j = 4 * lane + 256 * e4;
-          float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-          if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
-          xr[4 * e4 + 0] = t.x;
-          xr[4 * e4 + 1] = (j + 1 < nc) ? t.y : -INFINITY;
-          xr[4 * e4 + 2] = (j + 2 < nc) ? t.z : -INFINITY;
-          xr[4 * e4 + 3] = (j + 3 < nc) ? t.w : -INFINITY;
-        }
-      };
-      bool fallback;
-      uint32_t bz;
-      {
-        float xr[EPL];
-        load_row(xr);
-        bz = select_row_hist<EPL>(xr, (nc + 255) / 256, a.p, lane, whist[wave], &fallback);
-      }
-      if (fallback) {
-        float xr[EPL];
-        load_row(xr);
-        bz = select_row<EPL>(xr, a.p, lane);
-      }
-      bits[x] |= bz;
-    }
-    __syncthreads();  // the next branch overwrites the logits
   }
 
-  // ---- union of the branches -> mask rows, zeros included
+  const float kLog2e = 1.4426950408889634f;
+  const float *tau = a.tau + (int64_t)bh * 8;
+  const float ch = kLog2e / (tau[0] * sqrtf((float)a.d_high));
+  const float cl = kLog2e / (tau[1] * sqrtf((float)a.d_low));
+  float *ph = a.logits + (int64_t)bh * 2 * a.plane;
+  float *pl = ph + a.plane;
+  const int j = j0 + r32;
+  // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with key block j
 #pragma unroll
-  for (int x = 0; x < RPW; ++x) {
-    const int r = wave + kWaves * x;
-    const int i = i0 + r;
-    if (r >= RT || i >= nb) continue;
-    uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * nb + i) * nb;
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
+      const float mid = a.overlap ? acc1[r] : 0.f;
+      const int64_t o = logit_row(i, a.nb, a.causal) + j;
+      ph[o] = (acc0[r] + mid) * ch;
+      pl[o] = (acc2[r] + mid) * cl;
+    }
+  }
+}
+
+// One workgroup = two rows (batch, head, query block) x two branches: wave w
+// selects branch w % 2 of row w / 2; the branch pairs meet in LDS and the
+// even wave writes the union as the mask row. Rows are taken longest first.
+template <int EPL>
+__global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
+  __shared__ WaveHist whist[4];
+  __shared__ uint32_t sel_s[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int z = wave & 1;
+  const int nbh = a.batch * a.hq;
+  const int rid = blockIdx.x * 2 + (wave >> 1);
+  const bool live = rid < nbh * a.nb;
+  const int rr = live ? rid : 0;
+  const int i = a.causal ? a.nb - 1 - rr / nbh : rr / nbh;
+  const int bh = rr % nbh;
+  const int nc = a.causal ? i + 1 : a.nb;
+  const float *row = a.logits + ((int64_t)bh * 2 + z) * a.plane + logit_row(i, a.nb, a.causal);
+
+  auto load_row = [&](float (&xr)[EPL]) {
 #pragma unroll
     for (int e4 = 0; e4 < EPL / 4; ++e4) {
       const int j = 4 * lane + 256 * e4;
-      const uint32_t nib = (bits[x] >> (4 * e4)) & 0xFu;
-      if ((nb & 3) == 0) {
-        if (j < nb) {
-          const uint32_t word = (nib & 1u) | ((nib >> 1) & 1u) << 8 | ((nib >> 2) & 1u) << 16 | ((nib >> 3) & 1u) << 24;
-          *reinterpret_cast<uint32_t *>(mrow + j) = word;
-        }
-      } else {
+      float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
+      xr[4 * e4 + 0] = t.x;
+      xr[4 * e4 + 1] = (j + 1 < nc) ? t.y : -INFINITY;
+      xr[4 * e4 + 2] = (j + 2 < nc) ? t.z : -INFINITY;
+      xr[4 * e4 + 3] = (j + 3 < nc) ? t.w : -INFINITY;
+    }
+  };
+
+  uint32_t bits = 0;
+  if (live) {
+    bool fallback;
+    {
+      float xr[EPL];
+      load_row(xr);
+      bits = select_row_hist<EPL>(xr, (nc + 255) / 256, a.p, lane, whist[wave], &fallback);
+    }
+    if (fallback) {
+      float xr[EPL];
+      load_row(xr);
+      bits = select_row<EPL>(xr, a.p, lane);
+    }
+  }
+  sel_s[wave][lane] = bits;
+  __syncthreads();
+  if (!live || z != 0) return;
+  bits |= sel_s[wave + 1][lane];
+
+  // union of the branches -> mask row, zeros included
+  uint8_t *mrow = a.mask + ((int64_t)bh * a.nb + i) * a.nb;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (j + m < nb) mrow[j + m] = (uint8_t)((nib >> m) & 1u);
+  for (int e4 = 0; e4 < EPL / 4; ++e4) {
+    const int j = 4 * lane + 256 * e4;
+    const uint32_t nib = (bits >> (4 * e4)) & 0xFu;
+    if ((a.nb & 3) == 0) {
+      if (j < a.nb) {
+        const uint32_t word = (nib & 1u) | ((nib >> 1) & 1u) << 8 | ((nib >> 2) & 1u) << 16 | ((nib >> 3) & 1u) << 24;
+        *reinterpret_cast<uint32_t *>(mrow + j) = word;
       }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (j + m < a.nb) mrow[j + m] = (uint8_t)((nib >> m) & 1u);
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  if (a.nb <= 1024) {
-    constexpr int RT = 16;
-    const int ntiles = (a.nb + RT - 1) / RT;
-    hipLaunchKernelGGL((select_kernel<RT, 16>), dim3(ntiles * a.hq * a.batch), dim3(kThreads), 0, s, a);
-  } else {
-    constexpr int RT = 8;
-    const int ntiles = (a.nb + RT - 1) / RT;
-    hipLaunchKernelGGL((select_kernel<RT, 32>), dim3(ntiles * a.hq * a.batch), dim3(kThreads), 0, s, a);
-  }
+hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
+  const int nI = (a.nb + 63) / 64;
+  const int tiles = a.causal ? nI * (nI + 1) / 2 : nI * nI;
+  hipLaunchKernelGGL(score_kernel, dim3(tiles * a.hq * a.batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {
+  const int rows = a.batch * a.hq * a.nb;
+  const dim3 grid((rows + 1) / 2);
+  if (a.nb <= 1024) hipLaunchKernelGGL((topp_kernel<16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 1
+#define PRISM_ABI_VERSION 2
 
 typedef enum {
   PRISM_OK = 0,
@@ -115,6 +115,13 @@ typedef struct {
   size_t ksq_offset;  /* fp32 [batch][Hkv][nb][4] */
   size_t tau_offset;  /* fp32 [batch][Hq][8]: tau_high, tau_low, Rq_high, Rq_low, Rq_full,
                          Rk_high, Rk_low, Rk_full */
+  size_t logits_offset; /* fp32 [batch][Hq][2][logits_plane]: branch z's (0 high, 1 low) logits
+                         L_z[i][j] in log2 units, log2(e) Qbar_z[i].Kbar_z[j] / (tau_z sqrt(d_z)).
+                         causal: packed lower triangle, row i holds j = 0..i and starts at
+                         8 Q (Q + 1) + 4 R (Q + 1) floats (Q = i / 4, R = i % 4; rows padded to
+                         4 floats); otherwise row i holds all nb blocks and starts at
+                         i * round_up(nb, 4). */
+  int64_t logits_plane; /* floats between consecutive logit planes (a multiple of 64) */
   size_t total_bytes; /* == prism_estimate_workspace_bytes() */
   int64_t nb;         /* blocks per sequence, ceil(seq / block_size) */
   int32_t seg_lo, seg_hi, overlap, reserved;

@@ -110,3 +110,12 @@ def gpu_to_np_mask(m) -> np.ndarray:
 def bf16_tensor_to_f64(t) -> np.ndarray:
     import torch
     return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else t.cpu().numpy().astype(np.float64)
+
+
+def logit_row(i, nb, causal):
+    """start (floats) of row i of a logit plane: packed lower triangle with
+    rows padded to 4 floats when causal, rows of round_up(nb, 4) otherwise"""
+    if not causal:
+        return i * ((nb + 3) // 4 * 4)
+    q, r = i // 4, i % 4
+    return 8 * q * (q + 1) + 4 * r * (q + 1)

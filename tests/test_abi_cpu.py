@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 1
+    assert lib.prism_abi_version() == 2
     for s in range(10):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
@@ -76,6 +76,20 @@ def attn(lib, q, k, v, m, o):
     return lib.prism_block_sparse_attn(r(q), r(k), r(v), r(m), r(o), None)
 
 
+def test_logit_plane_rows_disjoint_and_padded():
+    """the documented packed-triangle row starts: row i holds i + 1 floats,
+    starts 16-byte aligned, and rows neither overlap nor leave a row short"""
+    from tests.parity import logit_row
+    for nb in (1, 2, 5, 8, 1023, 2048):
+        prev_end = 0
+        for i in range(nb):
+            s = logit_row(i, nb, True)
+            assert s % 4 == 0 and s >= prev_end
+            prev_end = s + -(-(i + 1) // 4) * 4
+        assert logit_row(nb, nb, True) == prev_end
+        assert logit_row(3, nb, False) == 3 * (-(-nb // 4) * 4)
+
+
 def test_workspace_layout(lib):
     q, k = tensor(seq=1000, heads=32), tensor(seq=1000, heads=8)
     L = PrismWorkspaceLayout()
@@ -87,7 +101,13 @@ def test_workspace_layout(lib):
     assert L.tau_offset >= L.ksq_offset + 8 * nb * 16
     assert L.total_bytes >= L.tau_offset + 32 * 32 and L.total_bytes % 256 == 0
     assert all(o % 256 == 0 for o in (L.kbar_offset, L.qsq_offset, L.ksq_offset, L.tau_offset))
+    # logit planes: 8 blocks, causal -> rows 0..7 packed with 4-float padding = 48 floats, plane 64
+    assert L.logits_plane == 64 and L.logits_offset % 256 == 0
+    assert L.logits_offset >= L.tau_offset + 32 * 32
+    assert L.total_bytes >= L.logits_offset + 32 * 2 * 64 * 4
     assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg())) == L.total_bytes
+    lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(causal=0)), ctypes.byref(L))
+    assert L.logits_plane == 64  # 8 rows of 8 floats
     # a gap between the bands: the middle segment belongs to neither
     lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(d_high=32, d_low=48)),
                                         ctypes.byref(L))

@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 import block_sparse_attention_band_amd as prism  # noqa: E402
 import oracle.prism_oracle as po  # noqa: E402
 from synth import WORKLOADS, make_qkv, random_mask, to_f64  # noqa: E402
-from tests.parity import compare_masks, oracle_estimate_heads, to_device  # noqa: E402
+from tests.parity import compare_masks, logit_row, oracle_estimate_heads, to_device  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,17 @@ def cfg_of(w, **kw):
 def read_ws(ws, off, shape):
     n = int(np.prod(shape))
     return ws[off: off + 4 * n].view(torch.float32).reshape(shape).cpu().numpy().astype(np.float64)
+
+
+def read_logits(ws, L, bh, z, causal):
+    """one logit plane as a dense [nb, nb] array, -inf where nothing is stored"""
+    nb = int(L.nb)
+    plane = read_ws(ws, L.logits_offset + (2 * bh + z) * L.logits_plane * 4, (int(L.logits_plane),))
+    out = np.full((nb, nb), -np.inf)
+    for i in range(nb):
+        n = i + 1 if causal else nb
+        out[i, :n] = plane[logit_row(i, nb, causal): logit_row(i, nb, causal) + n]
+    return out
 
 
 def canonical(x, rope_layout):
@@ -105,6 +116,15 @@ def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=
             assert np.allclose(tau[bb, h, :2], r["tau"], rtol=2e-5, atol=0), (tau[bb, h, :2], r["tau"])
             assert np.allclose(tau[bb, h, 2:5], r["rms_q"], rtol=2e-5, atol=0)
             assert np.allclose(tau[bb, h, 5:8], r["rms_k"], rtol=2e-5, atol=0)
+            # band logits, log2 units, on the admissible entries
+            for z, key in enumerate(("L_high", "L_low")):
+                gl = read_logits(ws, L, bb * w.hq + h, z, cfg.causal)
+                ol = r[key] * np.log2(np.e)
+                adm = np.isfinite(ol)
+                assert np.array_equal(adm, np.isfinite(gl)), (bb, h, z)
+                tol = 2e-5 * max(1.0, np.abs(ol[adm]).max())
+                err = np.abs(gl[adm] - ol[adm]).max()
+                assert err <= tol, (bb, h, z, err, tol)
     st = compare_masks(gm, orc, cfg.p, cfg.causal)
     dens = gm.sum() / max(1, st["blocks"])
     say(f"    density={dens:.4f} blocks={st['blocks']} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
