@@ -79,8 +79,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
   const int tp = tid / lanes_per_tok;
   const int hh = (tid % lanes_per_tok) / TPH;
   const int dg = tid % TPH;
-  const int h = chunk * HC + hh;
-  const bool active = tp < tokp && h < x.heads;
+  const int h = a.h0[ts] + chunk * HC + hh;
+  const bool active = tp < tokp && h < a.h0[ts] + a.nheads[ts];
 
   const int t0 = i * a.block;
   const int n = min(a.block, a.seq - t0);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
 
 __global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
   __shared__ double red[6][kThreads];
-  const int h = blockIdx.x;
+  const int h = a.h0 + blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / (a.hq / a.hkv);
   const float4 *qs = reinterpret_cast<const float4 *>(a.qsq) + ((int64_t)b * a.hq + h) * a.nb;
@@ -215,7 +215,7 @@ hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s) {
 }
 
 hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(tau_kernel, dim3(a.hq, batch), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(tau_kernel, dim3(a.nh, batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

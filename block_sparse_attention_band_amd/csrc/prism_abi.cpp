@@ -164,14 +164,7 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
 
   prism::PoolArgs pa;
   const prism_tensor_t *xs[2] = {q, k};
-  const int per_chunk_max = fp32 ? 8 : 16;  // heads one 256-thread workgroup covers per token
-  for (int t = 0; t < 2; ++t) {
-    pa.x[t] = targ(xs[t]);
-    const int H = (int)xs[t]->heads;
-    const int hc = H < per_chunk_max ? H : per_chunk_max;
-    pa.heads_per_chunk[t] = hc;
-    pa.chunks[t] = (H + hc - 1) / hc;
-  }
+  for (int t = 0; t < 2; ++t) pa.x[t] = targ(xs[t]);
   pa.xbar[0] = reinterpret_cast<float *>(ws + L.qbar_offset);
   pa.xbar[1] = reinterpret_cast<float *>(ws + L.kbar_offset);
   pa.sq[0] = reinterpret_cast<float *>(ws + L.qsq_offset);
@@ -222,6 +215,17 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   tp.causal = cfg->causal;
   tp.p = cfg->p;
 
+  const int per_chunk_max = fp32 ? 8 : 16;  // heads one 256-thread workgroup covers per token
+  const int nh[2] = {ta.hq, ta.hkv};
+  for (int t = 0; t < 2; ++t) {
+    const int hc = nh[t] < per_chunk_max ? nh[t] : per_chunk_max;
+    pa.h0[t] = 0;
+    pa.nheads[t] = nh[t];
+    pa.heads_per_chunk[t] = hc;
+    pa.chunks[t] = (nh[t] + hc - 1) / hc;
+  }
+  ta.h0 = sc.h0 = tp.h0 = 0;
+  ta.nh = sc.nh = tp.nh = ta.hq;
   if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (prism::launch_score(sc, s) != hipSuccess) return PRISM_ERR_LAUNCH;

@@ -23,6 +23,8 @@ struct PoolArgs {
   TensorArg x[2];        // 0 = Q, 1 = K
   float *xbar[2];        // [batch][heads][nb][128], canonical frequency order
   float *sq[2];          // [batch][heads][nb][4]
+  int32_t h0[2];         // first head of the range pooled, per tensor
+  int32_t nheads[2];     // heads in the range
   int32_t chunks[2];     // head chunks per tensor
   int32_t heads_per_chunk[2];
   int32_t seq, nb, block;
@@ -34,6 +36,7 @@ struct TauArgs {
   const float *qsq, *ksq;  // [batch][H][nb][4]
   float *tau;              // [batch][Hq][8]
   int32_t hq, hkv, nb;
+  int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
   int32_t d_high, d_low, overlap;
   int32_t tau_none;
 };
@@ -56,6 +59,7 @@ struct ScoreArgs {
   float *logits;           // [batch][Hq][2][plane]
   int64_t plane;
   int32_t hq, hkv, nb, batch;
+  int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
   int32_t seg_lo, seg_hi, overlap;
   int32_t d_high, d_low;
   int32_t causal;
@@ -66,6 +70,7 @@ struct TopPArgs {
   uint8_t *mask;           // [batch][Hq][nb][nb]
   int64_t plane;
   int32_t hq, nb, batch;
+  int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
   int32_t causal;
   float p;
 };

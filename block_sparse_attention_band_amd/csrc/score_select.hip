@@ -458,89 +458,151 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 // segment of canonical dim d: 0 high-only, 1 middle, 2 low-only
 __device__ __forceinline__ int seg_of(int d, int lo, int hi) { return d < lo ? 0 : (d < hi ? 1 : 2); }
 
-// One workgroup = one 64 x 64 tile (query blocks I*64.., key blocks J*64..)
-// of one head; wave w owns the 32 x 32 quadrant (w / 2, w % 2). MFMA operands:
-// lane l gives query row l % 32 and key row l % 32 of its quadrant, and the
-// dims 8c + 4(l / 32) + e for the MFMA e of chunk c; A and B use the same
-// dim for the same k, so each chunk's 8 dims are summed exactly once.
-__global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
-  const int nI = (a.nb + 63) / 64;
-  const int tiles = a.causal ? nI * (nI + 1) / 2 : nI * nI;
-  const int bh = blockIdx.x / tiles;
-  const int t = blockIdx.x % tiles;
-  int I, J;
-  if (a.causal) {
-    I = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while ((I + 1) * (I + 2) / 2 <= t) ++I;
-    while (I * (I + 1) / 2 > t) --I;
-    J = t - I * (I + 1) / 2;
-  } else {
-    I = t / nI;
-    J = t % nI;
-  }
-  const int b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r32 = lane & 31, hf = lane >> 5;
-  const int i0 = I * 64 + 32 * (wave >> 1), j0 = J * 64 + 32 * (wave & 1);
-  if (i0 >= a.nb || j0 >= a.nb) return;
-  if (a.causal && j0 > i0 + 31) return;  // quadrant entirely above the diagonal
+constexpr int kScoreTilesPerWg = 4;  // key tiles one workgroup sweeps along its strip
 
-  const float *qp = a.qbar + ((int64_t)bh * a.nb + min(i0 + r32, a.nb - 1)) * kHeadDim + 4 * hf;
-  const float *kp = a.kbar + (((int64_t)b * a.hkv + g) * a.nb + min(j0 + r32, a.nb - 1)) * kHeadDim + 4 * hf;
-  float4 qa[16], ka[16];
+// Accumulates the 16 dim chunks of one tile into the segment accumulators.
+// Chunk c holds canonical dims 8c..8c+7; lane half hf supplies dims
+// 8c + 4hf + e for MFMA e (A and B agree, so each dim enters once).
+// LO8, HI8 >= 0: both segment boundaries are multiples of 8 (lo = 8 LO8,
+// hi = 8 HI8), every chunk lies in one segment known at compile time.
+// Otherwise each chunk feeds all three accumulators with the dims of the
+// other segments zeroed (three times the MFMAs, for unusual band widths).
+template <int LO8, int HI8>
+__device__ __forceinline__ void score_tile(const float4 (&qa)[16], const float4 *kr, int krow, int hf, int lo, int hi,
+                                           int overlap, f32x16 &acc0, f32x16 &acc1, f32x16 &acc2) {
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
-    qa[c] = *reinterpret_cast<const float4 *>(qp + 8 * c);
-    ka[c] = *reinterpret_cast<const float4 *>(kp + 8 * c);
-  }
-  f32x16 acc0, acc1, acc2;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; acc2[r] = 0.f; }
-  const int lo = a.seg_lo, hi = a.seg_hi;
-  // Each accumulator has its own (wave-uniform) branch per chunk, so no
-  // accumulator is ever selected at run time. A chunk inside one segment
-  // feeds that segment only; a chunk across a boundary feeds each segment it
-  // touches with the other segments' dims zeroed.
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
+    const float4 k4 = kr[(2 * c + hf) ^ (krow & 15)];
     const float qv[4] = {qa[c].x, qa[c].y, qa[c].z, qa[c].w};
-    const float kv[4] = {ka[c].x, ka[c].y, ka[c].z, ka[c].w};
-    const bool t0 = 8 * c < lo;
-    const bool t1 = a.overlap && 8 * c + 7 >= lo && 8 * c < hi;
-    const bool t2 = 8 * c + 7 >= hi;
-    const bool whole = seg_of(8 * c, lo, hi) == seg_of(8 * c + 7, lo, hi);
+    const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+    if constexpr (LO8 >= 0) {
+      if (c < LO8) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int sd = seg_of(8 * c + 4 * hf + e, lo, hi);
-      if (t0) acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 0) ? qv[e] : 0.f, kv[e], acc0, 0, 0, 0);
-      if (t1) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 1) ? qv[e] : 0.f, kv[e], acc1, 0, 0, 0);
-      if (t2) acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32((whole || sd == 2) ? qv[e] : 0.f, kv[e], acc2, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[e], kv[e], acc0, 0, 0, 0);
+      } else if (c < HI8) {
+        if (overlap) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[e], kv[e], acc1, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[e], kv[e], acc2, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sd = seg_of(8 * c + 4 * hf + e, lo, hi);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sd == 0 ? qv[e] : 0.f, kv[e], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sd == 1 && overlap ? qv[e] : 0.f, kv[e], acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sd == 2 ? qv[e] : 0.f, kv[e], acc2, 0, 0, 0);
+      }
     }
   }
+}
+
+// One workgroup = query blocks I*64..I*64+63 of one head against up to
+// kScoreTilesPerWg consecutive 64-key-block tiles of its strip. Wave w owns
+// the 32 x 32 quadrant (w / 2, w % 2) of each tile. The wave's 32 Qbar rows
+// stay in registers (lane l: row l % 32, dims 8c + 4(l / 32)..+3 of chunk c);
+// Kbar tiles (64 x 128 fp32) stream through two LDS buffers, the next tile's
+// global loads in flight while the current one is computed. LDS rows are 512
+// bytes; 16-byte slot s of row r sits at s ^ (r % 16), so the 16 rows one
+// ds_read_b128 pass touches fall in 16 different bank groups.
+template <int LO8, int HI8>
+__global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) float4 kt[2][64 * 32];
+  const int nI = (a.nb + 63) / 64;
+  // work item -> (head, strip I, tile chunk)
+  int per_head = 0;
+  for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
+  const int lbh = blockIdx.x / per_head;  // (batch, head within the range)
+  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+  int w = blockIdx.x % per_head, I = 0;
+  for (;; ++I) {
+    const int n = ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
+    if (w < n) break;
+    w -= n;
+  }
+  const int nJ = a.causal ? I + 1 : nI;
+  const int J0 = w * kScoreTilesPerWg, J1 = min(nJ, J0 + kScoreTilesPerWg);
+
+  const int b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, hf = lane >> 5;
+  const int i0 = I * 64 + 32 * (wave >> 1);
+  const int lo = a.seg_lo, hi = a.seg_hi;
+
+  // the wave's Qbar rows
+  float4 qa[16];
+  {
+    const float *qp = a.qbar + ((int64_t)bh * a.nb + min(i0 + r32, a.nb - 1)) * kHeadDim + 4 * hf;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qa[c] = *reinterpret_cast<const float4 *>(qp + 8 * c);
+  }
+  // tile staging: thread t moves float4 u = t + 256 x of the tile (row u / 32,
+  // 16-byte slot u % 32); the row index is clamped at the sequence end
+  const float *kbase = a.kbar + ((int64_t)b * a.hkv + g) * a.nb * kHeadDim;
+  const int srow = tid >> 5, sslot = tid & 31;  // x adds 8 rows
+#define PRISM_LOAD_TILE(J)                                                                                   \
+  _Pragma("unroll") for (int x = 0; x < 8; ++x) pre[x] = *reinterpret_cast<const f32x4v *>(                \
+      kbase + (int64_t)min((J) * 64 + srow + 8 * x, a.nb - 1) * kHeadDim + 4 * sslot);
+#define PRISM_STORE_TILE(buf)                                                                                \
+  _Pragma("unroll") for (int x = 0; x < 8; ++x)                                                              \
+      *reinterpret_cast<f32x4v *>(&(buf)[(srow + 8 * x) * 32 + (sslot ^ ((srow + 8 * x) & 15))]) = pre[x];
 
   const float kLog2e = 1.4426950408889634f;
   const float *tau = a.tau + (int64_t)bh * 8;
   const float ch = kLog2e / (tau[0] * sqrtf((float)a.d_high));
   const float cl = kLog2e / (tau[1] * sqrtf((float)a.d_low));
   float *ph = a.logits + (int64_t)bh * 2 * a.plane;
-  float *pl = ph + a.plane;
-  const int j = j0 + r32;
-  // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with key block j
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = i0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-    if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
-      const float mid = a.overlap ? acc1[r] : 0.f;
-      const int64_t o = logit_row(i, a.nb, a.causal) + j;
-      ph[o] = (acc0[r] + mid) * ch;
-      pl[o] = (acc2[r] + mid) * cl;
-    }
+  const int krow = 32 * (wave & 1) + r32;  // this lane's key row within a tile
+
+  {
+    f32x4v pre[8];
+    PRISM_LOAD_TILE(J0)
+    PRISM_STORE_TILE(kt[0])
   }
+  // Qbar and the first tile have landed: s_waitcnt vmcnt(0), so that the
+  // loop's waits only ever cover its own prefetch
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int J = J0; J < J1; ++J) {
+    const int cur = (J - J0) & 1;
+    const bool more = J + 1 < J1;
+    f32x4v pre[8];
+    if (more) { PRISM_LOAD_TILE(J + 1) }
+    // keep the next tile's loads here, ahead of this tile's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    const int j0 = J * 64 + 32 * (wave & 1);
+    if (i0 < a.nb && j0 < a.nb && !(a.causal && j0 > i0 + 31)) {
+      f32x16 acc0, acc1, acc2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; acc2[r] = 0.f; }
+      score_tile<LO8, HI8>(qa, kt[cur] + krow * 32, krow, hf, lo, hi, a.overlap, acc0, acc1, acc2);
+      const int j = j0 + r32;
+      // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with key block j
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
+          const float mid = a.overlap ? acc1[r] : 0.f;
+          const int64_t o = logit_row(i, a.nb, a.causal) + j;
+          ph[o] = (acc0[r] + mid) * ch;
+          ph[o + a.plane] = (acc2[r] + mid) * cl;
+        }
+      }
+    }
+    if (more) { PRISM_STORE_TILE(kt[cur ^ 1]) }
+    __syncthreads();
+  }
+#undef PRISM_LOAD_TILE
+#undef PRISM_STORE_TILE
 }
 
 // One workgroup = two rows (batch, head, query block) x two branches: wave w
@@ -553,12 +615,13 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int z = wave & 1;
-  const int nbh = a.batch * a.hq;
+  const int nbh = a.batch * a.nh;
   const int rid = blockIdx.x * 2 + (wave >> 1);
   const bool live = rid < nbh * a.nb;
   const int rr = live ? rid : 0;
   const int i = a.causal ? a.nb - 1 - rr / nbh : rr / nbh;
-  const int bh = rr % nbh;
+  const int lbh = rr % nbh;
+  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
   const int nc = a.causal ? i + 1 : a.nb;
   const float *row = a.logits + ((int64_t)bh * 2 + z) * a.plane + logit_row(i, a.nb, a.causal);
 
@@ -617,13 +680,18 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   const int nI = (a.nb + 63) / 64;
-  const int tiles = a.causal ? nI * (nI + 1) / 2 : nI * nI;
-  hipLaunchKernelGGL(score_kernel, dim3(tiles * a.hq * a.batch), dim3(256), 0, s, a);
+  int per_head = 0;
+  for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
+  const dim3 grid(per_head * a.nh * a.batch);
+  if (a.seg_lo == 32 && a.seg_hi == 64) hipLaunchKernelGGL((score_kernel<4, 8>), grid, dim3(256), 0, s, a);
+  else if (a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0 && a.seg_lo == 0 && a.seg_hi == 128)
+    hipLaunchKernelGGL((score_kernel<0, 16>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((score_kernel<-1, -1>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {
-  const int rows = a.batch * a.hq * a.nb;
+  const int rows = a.batch * a.nh * a.nb;
   const dim3 grid((rows + 1) / 2);
   if (a.nb <= 1024) hipLaunchKernelGGL((topp_kernel<16>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);

@@ -155,6 +155,7 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  * Work: two streaming reads of Q and K (block means and segment energies),
  * a per-head temperature reduction, and per query block the two band score
  * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
+ * Four kernels, in order on `stream`.
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream);
