@@ -224,10 +224,12 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
     pa.heads_per_chunk[t] = hc;
     pa.chunks[t] = (nh[t] + hc - 1) / hc;
   }
-  ta.h0 = sc.h0 = tp.h0 = 0;
-  ta.nh = sc.nh = tp.nh = ta.hq;
+  ta.h0 = 0;
+  ta.nh = ta.hq;
   if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  sc.h0 = tp.h0 = 0;
+  sc.nh = tp.nh = ta.hq;
   if (prism::launch_score(sc, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (prism::launch_topp(tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   return PRISM_OK;

@@ -297,11 +297,14 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
   }
 
   // key = bit pattern of e (exp2(-inf) = 0 marks an entry that is not
-  // admissible; an e that underflows to 0 is never needed since p * Z <= Z)
+  // admissible; an e that underflows to 0 is never needed since p * Z <= Z).
+  // The first histogram pass runs while the keys are made.
   uint32_t key[EPL];
-  uint32_t act = 0;  // entries still undecided
 #pragma unroll
   for (int k = 0; k < EPL; ++k) key[k] = 0u;
+  Radix R;
+  H.bin[lane] = 0ull;
+  wave_lds_sync();
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
     if (e4 >= ne4) break;
@@ -309,27 +312,32 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
     for (int m = 0; m < 4; ++m) {
       const int k = 4 * e4 + m;
       key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
-      act |= (key[k] ? 1u : 0u) << k;
+      if (key[k]) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
     }
   }
   unsigned long long Z = 0, target = 0, before = 0;
-  uint32_t sel = 0, c = 0;
-  Radix R;
+  uint32_t sel = 0, c = 0, act = 0;
   int bstar = 0;
   for (int level = 0;; ++level) {
-    H.bin[lane] = 0ull;
-    wave_lds_sync();
+    if (level > 0) {
+      H.bin[lane] = 0ull;
+      wave_lds_sync();
 #pragma unroll
-    for (int e4 = 0; e4 < EPL / 4; ++e4) {
-      if (e4 >= ne4) break;
+      for (int e4 = 0; e4 < EPL / 4; ++e4) {
+        if (e4 >= ne4) break;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = 4 * e4 + m;
-        if ((act >> k) & 1u) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
+        for (int m = 0; m < 4; ++m) {
+          const int k = 4 * e4 + m;
+          if ((act >> k) & 1u) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
+        }
       }
     }
     bstar = Hist::pass_done(H, lane, p, Z, target, before, &c);
     wave_lds_sync();
+    // bins above b* hold keys >= hi_key, b* holds [lo_key, hi_key) (the tail
+    // bin everything below hi_key); at level 0 every nonzero key is undecided
+    const uint32_t hi_key = (uint32_t)(R.base - bstar + 1) << R.shift;
+    const uint32_t lo_key = (R.tail && bstar == 63) ? 1u : (uint32_t)(R.base - bstar) << R.shift;
     uint32_t nact = 0;
 #pragma unroll
     for (int e4 = 0; e4 < EPL / 4; ++e4) {
@@ -337,11 +345,9 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int k = 4 * e4 + m;
-        if ((act >> k) & 1u) {
-          const int bk = R.bin(key[k]);
-          if (bk < bstar) sel |= 1u << k;
-          if (bk == bstar) nact |= 1u << k;
-        }
+        const bool undecided = level == 0 ? key[k] != 0u : ((act >> k) & 1u) != 0u;
+        if (undecided && key[k] >= hi_key) sel |= 1u << k;
+        if (undecided && key[k] >= lo_key && key[k] < hi_key) nact |= 1u << k;
       }
     }
     act = nact;
@@ -517,19 +523,37 @@ template <int LO8, int HI8>
 __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) float4 kt[2][64 * 32];
   const int nI = (a.nb + 63) / 64;
-  // work item -> (head, strip I, tile chunk)
-  int per_head = 0;
-  for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
-  const int lbh = blockIdx.x / per_head;  // (batch, head within the range)
+  constexpr int T = kScoreTilesPerWg;
+  // Work item -> (head, strip I, tile chunk). Per head, the chunks of T tiles
+  // come first (longest strips first), then the shorter remainders; the heads
+  // of one chunk rank are adjacent in the grid, so the long work starts first.
+  const int nbh = a.batch * a.nh;
+  const int lbh = blockIdx.x % nbh;
   const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
-  int w = blockIdx.x % per_head, I = 0;
-  for (;; ++I) {
-    const int n = ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
-    if (w < n) break;
-    w -= n;
+  int w = blockIdx.x / nbh, I = nI - 1, J0 = 0, J1 = 0;
+  int nfull = 0;
+  for (int t = 0; t < nI; ++t) nfull += (a.causal ? t + 1 : nI) / T;
+  if (w < nfull) {
+    for (;; --I) {
+      const int nf = (a.causal ? I + 1 : nI) / T;
+      if (w < nf) break;
+      w -= nf;
+    }
+    J0 = w * T;
+    J1 = J0 + T;
+  } else {
+    w -= nfull;
+    for (;; --I) {
+      const int nJ = a.causal ? I + 1 : nI;
+      if (nJ % T == 0) continue;
+      if (w == 0) {
+        J0 = nJ - nJ % T;
+        J1 = nJ;
+        break;
+      }
+      --w;
+    }
   }
-  const int nJ = a.causal ? I + 1 : nI;
-  const int J0 = w * kScoreTilesPerWg, J1 = min(nJ, J0 + kScoreTilesPerWg);
 
   const int b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -561,6 +585,8 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
   const float ch = kLog2e / (tau[0] * sqrtf((float)a.d_high));
   const float cl = kLog2e / (tau[1] * sqrtf((float)a.d_low));
   float *ph = a.logits + (int64_t)bh * 2 * a.plane;
+  float *pl = ph + a.plane;
+  const int nb4 = (a.nb + 3) & ~3;
   const int krow = 32 * (wave & 1) + r32;  // this lane's key row within a tile
 
   {
@@ -586,15 +612,24 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
       for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; acc2[r] = 0.f; }
       score_tile<LO8, HI8>(qa, kt[cur] + krow * 32, krow, hf, lo, hi, a.overlap, acc0, acc1, acc2);
       const int j = j0 + r32;
-      // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with key block j
+      // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with
+      // key block j; each group of 4 rows starts at a multiple of 4, so the
+      // 4 row starts are base + rr * step (32-bit offsets within the plane)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
-          const float mid = a.overlap ? acc1[r] : 0.f;
-          const int64_t o = logit_row(i, a.nb, a.causal) + j;
-          ph[o] = (acc0[r] + mid) * ch;
-          ph[o + a.plane] = (acc2[r] + mid) * cl;
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ib = i0 + 8 * gq + 4 * hf;
+        const int q4 = ib >> 2;
+        const int base = a.causal ? 8 * q4 * (q4 + 1) : ib * nb4;
+        const int step = a.causal ? 4 * (q4 + 1) : nb4;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = ib + rr, r = 4 * gq + rr;
+          if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
+            const float mid = a.overlap ? acc1[r] : 0.f;
+            const int o = base + rr * step + j;
+            ph[o] = (acc0[r] + mid) * ch;
+            pl[o] = (acc2[r] + mid) * cl;
+          }
         }
       }
     }
@@ -682,7 +717,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   const int nI = (a.nb + 63) / 64;
   int per_head = 0;
   for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
-  const dim3 grid(per_head * a.nh * a.batch);
+  const dim3 grid(per_head * a.nh * a.batch);  // heads x (full chunks, then remainders)
   if (a.seg_lo == 32 && a.seg_hi == 64) hipLaunchKernelGGL((score_kernel<4, 8>), grid, dim3(256), 0, s, a);
   else if (a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0 && a.seg_lo == 0 && a.seg_hi == 128)
     hipLaunchKernelGGL((score_kernel<0, 16>), grid, dim3(256), 0, s, a);
