@@ -26,7 +26,10 @@ GPU reads. Readings taken where the pages are silent:
   * RMS is taken over all pooled blocks of a head, per tensor and per band;
   * tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full))
     (the formula is named but not printed) -- parity unpinned against the
-    pages; tau = 1 if any R is 0;
+    pages; tau = 1 if any R is 0. Two rejected readings are kept for
+    comparison: 'unit' (tau_z = R(Qbar,D_z) R(Kbar,D_z), unit-energy
+    normalisation) and 'pervec' (the RMS taken per pooled vector, which scales
+    each block's band to the energy density of its own full spectrum);
   * causal softmax over key blocks j <= i; Top-P keeps the smallest set of
     highest scores whose mass reaches p (inclusive), ties by lower index;
   * attention scale 1/sqrt(d); a query with no admissible key outputs 0;
@@ -37,7 +40,7 @@ from __future__ import annotations
 import numpy as np
 
 ROPE_LAYOUTS = ("interleaved", "half")
-TAU_MODES = ("fullspec", "none")
+TAU_MODES = ("fullspec", "none", "unit", "pervec")
 
 
 # ---------------------------------------------------------------- step (1)
@@ -107,17 +110,37 @@ def temperature(qbar: np.ndarray, kbar: np.ndarray, dims_z: np.ndarray, dims_ful
     printed; the reading used here is the band's pooled energy relative to the
     full spectrum's, for query and key:
         tau_z = R(Qbar, D_z) R(Kbar, D_z) / (R(Qbar, D_full) R(Kbar, D_full)).
-    mode 'none' gives tau = 1 (plain pooled scores per band).
+    mode 'none' gives tau = 1 (plain pooled scores per band). Rejected
+    readings kept for comparison: 'unit', tau_z = R(Qbar, D_z) R(Kbar, D_z)
+    (unit-energy normalisation with no full-spectrum reference), and
+    'pervec', where the RMS is taken per pooled vector (pervec_factors) and
+    the head-level tau is 1.
     """
-    if mode == "none":
+    if mode in ("none", "pervec"):
         return 1.0, False
-    if mode != "fullspec":
+    if mode not in ("fullspec", "unit"):
         raise ValueError(mode)
     rq_z, rk_z = band_rms(qbar, dims_z), band_rms(kbar, dims_z)
     rq_f, rk_f = band_rms(qbar, dims_full), band_rms(kbar, dims_full)
     if min(rq_z, rk_z, rq_f, rk_f) == 0.0:
         return 1.0, True
+    if mode == "unit":
+        return rq_z * rk_z, False
     return (rq_z * rk_z) / (rq_f * rk_f), False
+
+
+def pervec_factors(xbar: np.ndarray, dims_z: np.ndarray, dims_full: np.ndarray) -> np.ndarray:
+    """Per-vector reading of the RMS calibration (Prism review, pipeline steps
+    (3)-(4), taken per pooled vector instead of per head): block i's band
+    z is scaled by R(xbar_i, D_full) / R(xbar_i, D_z), i.e. to the energy
+    density of its own full spectrum; 1 where R(xbar_i, D_z) is 0.
+    """
+    rz = np.sqrt(np.mean(xbar[:, dims_z] ** 2, axis=1))
+    rf = np.sqrt(np.mean(xbar[:, dims_full] ** 2, axis=1))
+    out = np.ones(xbar.shape[0])
+    nz = rz > 0
+    out[nz] = rf[nz] / rz[nz]
+    return out
 
 
 # ---------------------------------------------------------------- step (5)
@@ -127,16 +150,20 @@ def admissible(i: int, nb: int, causal: bool) -> np.ndarray:
 
 
 def band_scores(qbar: np.ndarray, kbar: np.ndarray, dims_z: np.ndarray, tau: float,
-                causal: bool) -> tuple[np.ndarray, np.ndarray]:
+                causal: bool, fq: np.ndarray | None = None, fk: np.ndarray | None = None
+                ) -> tuple[np.ndarray, np.ndarray]:
     """Logits L and block softmax S of one branch.
 
     Prism review, pipeline step (5):
         S_z = softmax(Qbar_z Kbar_z^T / (tau_z sqrt(d_z))),
     the softmax of row i taken over the admissible key blocks J(i) (j <= i when
-    causal). Entries outside J(i): L = -inf, S = 0.
+    causal). Entries outside J(i): L = -inf, S = 0. fq, fk (per-vector
+    reading only) scale row i by fq[i] and column j by fk[j].
     """
     nb = qbar.shape[0]
     L = (qbar[:, dims_z] @ kbar[:, dims_z].T) / (tau * np.sqrt(len(dims_z)))
+    if fq is not None:
+        L = L * fq[:, None] * fk[None, :]
     S = np.zeros_like(L)
     Lm = np.full_like(L, -np.inf)
     for i in range(nb):
@@ -200,8 +227,12 @@ def estimate_head(qh: np.ndarray, kg: np.ndarray, *, block: int, d_high: int, d_
         kbar = mean_pool(kg, block)
     tau_h, deg_h = temperature(qbar, kbar, hi, full, tau_mode)
     tau_l, deg_l = temperature(qbar, kbar, lo, full, tau_mode)
-    L_h, S_h = band_scores(qbar, kbar, hi, tau_h, causal)
-    L_l, S_l = band_scores(qbar, kbar, lo, tau_l, causal)
+    fh = fl = (None, None)
+    if tau_mode == "pervec":
+        fh = (pervec_factors(qbar, hi, full), pervec_factors(kbar, hi, full))
+        fl = (pervec_factors(qbar, lo, full), pervec_factors(kbar, lo, full))
+    L_h, S_h = band_scores(qbar, kbar, hi, tau_h, causal, *fh)
+    L_l, S_l = band_scores(qbar, kbar, lo, tau_l, causal, *fl)
     m_h = top_p_mask(S_h, p, causal)
     m_l = top_p_mask(S_l, p, causal)
     return {

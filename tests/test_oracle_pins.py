@@ -124,6 +124,74 @@ def test_tau_closed_form(rope_layout, d_high, d_low):
     assert tau_closed_form_error(rope_layout, d_high, d_low) < 1e-12
 
 
+def test_tau_unit_closed_form_and_pervec_equals_fullspec_on_constant_blocks():
+    """The rejected readings on the same construction: 'unit' gives
+    tau_z = R(Qbar,D_z) R(Kbar,D_z) = sum_{j in F_z} D^2 |x_j|^2 / |D_z|; every
+    pooled block is the same vector, so the per-vector RMS equals the head's
+    and 'pervec' logits equal the adopted reading's."""
+    d, B, nb, base = 128, 64, 5, 5e5
+    x = np.random.default_rng(0).standard_normal(d)
+    cos, sin = rope_tables(nb * B, d, base)
+    xr = apply_rope(np.tile(x, (nb * B, 1)), cos, sin, "interleaved")
+    kw = dict(block=B, d_high=64, d_low=96, p=0.9)
+    u = po.estimate_head(xr, xr, tau_mode="unit", **kw)
+    f = po.estimate_head(xr, xr, **kw)
+    v = po.estimate_head(xr, xr, tau_mode="pervec", **kw)
+    pair = dirichlet(B, freqs(d, base)) ** 2 * (x[0::2] ** 2 + x[1::2] ** 2)
+    assert abs(u["tau"][0] - pair[:32].sum() / 64) < 1e-12 * u["tau"][0]
+    assert abs(u["tau"][1] - pair[16:].sum() / 96) < 1e-12 * u["tau"][1]
+    assert v["tau"] == (1.0, 1.0)
+    for key in ("L_high", "L_low"):
+        fin = np.isfinite(f[key])
+        assert np.array_equal(fin, np.isfinite(v[key]))
+        assert np.abs(v[key][fin] - f[key][fin]).max() <= 1e-12 * np.abs(f[key][fin]).max()
+
+
+def test_tau_unit_logits_invariant_to_scaling_q_and_k():
+    """Unit-energy normalisation divides out the scale of Q and K."""
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal((700, 128)), rng.standard_normal((700, 128))
+    a = po.estimate_head(q, k, block=128, d_high=64, d_low=96, p=0.95, tau_mode="unit")
+    b = po.estimate_head(3.7 * q, 0.2 * k, block=128, d_high=64, d_low=96, p=0.95, tau_mode="unit")
+    fin = np.isfinite(a["L_high"])
+    for key in ("L_high", "L_low"):
+        assert np.allclose(a[key][fin], b[key][fin], rtol=1e-12, atol=0)
+    assert np.array_equal(a["mask"], b["mask"])
+
+
+def test_tau_pervec_is_band_rescaled_to_own_full_rms():
+    """Per-vector reading by another route: rescale each pooled vector's band
+    to the RMS of its own full spectrum, then take the plain band dot
+    product / sqrt(d_z)."""
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((900, 128)) * np.linspace(0.2, 2.0, 128)
+    k = rng.standard_normal((900, 128)) * np.linspace(2.0, 0.3, 128)
+    r = po.estimate_head(q, k, block=128, d_high=64, d_low=96, p=0.95, tau_mode="pervec", causal=False)
+    qb, kb = r["qbar"], r["kbar"]
+    for key, dims in (("L_high", np.arange(64)), ("L_low", np.arange(32, 128))):
+        qz = qb[:, dims] * (np.linalg.norm(qb, axis=1) / math.sqrt(128) /
+                            (np.linalg.norm(qb[:, dims], axis=1) / math.sqrt(len(dims))))[:, None]
+        kz = kb[:, dims] * (np.linalg.norm(kb, axis=1) / math.sqrt(128) /
+                            (np.linalg.norm(kb[:, dims], axis=1) / math.sqrt(len(dims))))[:, None]
+        want = qz @ kz.T / math.sqrt(len(dims))
+        assert np.abs(r[key] - want).max() <= 1e-12 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("mode", ["unit", "pervec"])
+def test_rejected_readings_reduce_to_plain_pooling_with_equal_bands(mode, monkeypatch):
+    """With D_z = D_full the per-vector factors are 1; 'unit' rescales both
+    branches alike, so both branches still select the same blocks."""
+    rng = np.random.default_rng(7)
+    q, k = rng.standard_normal((300, 128)), rng.standard_normal((300, 128))
+    base = po.estimate_head(q, k, block=32, d_high=128, d_low=128, p=0.8, tau_mode="none")
+    r = po.estimate_head(q, k, block=32, d_high=128, d_low=128, p=0.8, tau_mode=mode)
+    assert np.array_equal(r["m_high"], r["m_low"])
+    if mode == "pervec":
+        fin = np.isfinite(base["L_high"])
+        assert np.allclose(r["L_high"][fin], base["L_high"][fin], rtol=1e-12, atol=0)
+        assert np.array_equal(r["mask"], base["mask"])
+
+
 def test_tau_attenuated_high_band_is_amplified():
     """gist.science 2B: the high branch's pooled logits are attenuated, and the
     calibration restores them (tau_high < 1 divides the logits up)."""
@@ -378,8 +446,8 @@ def test_planted_half_layout_bands_caught(monkeypatch):
 def test_planted_missing_sqrt_d_caught(monkeypatch):
     good = po.band_scores
 
-    def no_sqrt(qbar, kbar, dims, tau, causal):
-        return good(qbar, kbar, dims, tau / math.sqrt(len(dims)), causal)
+    def no_sqrt(qbar, kbar, dims, tau, causal, fq=None, fk=None):
+        return good(qbar, kbar, dims, tau / math.sqrt(len(dims)), causal, fq, fk)
 
     monkeypatch.setattr(po, "band_scores", no_sqrt)
     assert plain_pooled_error(True) > 0
