@@ -20,7 +20,8 @@ __all__ = ["EstimatorConfig", "estimate", "block_sparse_attn", "workspace_bytes"
            "PrismError", "lib"]
 
 _ROPE = {"interleaved": _abi.ROPE_INTERLEAVED, "half": _abi.ROPE_HALF}
-_TAU = {"fullspec": _abi.TAU_FULLSPEC, "none": _abi.TAU_NONE}
+_TAU = {"fullspec": _abi.TAU_FULLSPEC, "none": _abi.TAU_NONE, "unit": _abi.TAU_UNIT,
+        "pervec": _abi.TAU_PERVEC}
 
 
 @dataclass(frozen=True)

@@ -21,7 +21,7 @@ STATUS_NAMES = ["PRISM_OK", "PRISM_ERR_NULL", "PRISM_ERR_DTYPE", "PRISM_ERR_SHAP
                 "PRISM_ERR_LAUNCH"]
 BF16, FP32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
-TAU_FULLSPEC, TAU_NONE = 0, 1
+TAU_FULLSPEC, TAU_NONE, TAU_UNIT, TAU_PERVEC = 0, 1, 2, 3
 
 
 class PrismTensor(ctypes.Structure):

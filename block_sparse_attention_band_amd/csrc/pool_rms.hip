@@ -193,10 +193,17 @@ __global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
       r[3 * t + 1] = sqrt((e2 + ov * e1) / (nb * a.d_low));
       r[3 * t + 2] = sqrt((e0 + e1 + e2) / (nb * kHeadDim));
     }
+    // FULLSPEC: band energy relative to the full spectrum; UNIT: band
+    // energy alone; NONE and PERVEC: 1 (PERVEC scales per pooled vector)
     double th = 1.0, tl = 1.0;
-    if (!a.tau_none) {
-      if (r[0] > 0 && r[3] > 0 && r[2] > 0 && r[5] > 0) th = (r[0] * r[3]) / (r[2] * r[5]);
-      if (r[1] > 0 && r[4] > 0 && r[2] > 0 && r[5] > 0) tl = (r[1] * r[4]) / (r[2] * r[5]);
+    const bool okh = r[0] > 0 && r[3] > 0 && r[2] > 0 && r[5] > 0;
+    const bool okl = r[1] > 0 && r[4] > 0 && r[2] > 0 && r[5] > 0;
+    if (a.tau_mode == 0) {
+      if (okh) th = (r[0] * r[3]) / (r[2] * r[5]);
+      if (okl) tl = (r[1] * r[4]) / (r[2] * r[5]);
+    } else if (a.tau_mode == 2) {
+      if (okh) th = r[0] * r[3];
+      if (okl) tl = r[1] * r[4];
     }
     float *out = a.tau + ((int64_t)b * a.hq + h) * 8;
     out[0] = (float)th; out[1] = (float)tl;

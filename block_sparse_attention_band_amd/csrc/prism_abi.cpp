@@ -65,7 +65,7 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (!(cfg->p > 0.0f && cfg->p <= 1.0f)) return PRISM_ERR_CONFIG;
   if (cfg->causal != 0 && cfg->causal != 1) return PRISM_ERR_CONFIG;
   if (cfg->rope_layout != PRISM_ROPE_INTERLEAVED && cfg->rope_layout != PRISM_ROPE_HALF) return PRISM_ERR_CONFIG;
-  if (cfg->tau_mode != PRISM_TAU_FULLSPEC && cfg->tau_mode != PRISM_TAU_NONE) return PRISM_ERR_CONFIG;
+  if (cfg->tau_mode < PRISM_TAU_FULLSPEC || cfg->tau_mode > PRISM_TAU_PERVEC) return PRISM_ERR_CONFIG;
   if (cfg->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
   if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
@@ -186,7 +186,7 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   ta.d_high = cfg->d_high;
   ta.d_low = cfg->d_low;
   ta.overlap = L.overlap;
-  ta.tau_none = cfg->tau_mode == PRISM_TAU_NONE;
+  ta.tau_mode = cfg->tau_mode;
 
   prism::ScoreArgs sc;
   sc.qbar = pa.xbar[0];
@@ -204,6 +204,9 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   sc.d_high = cfg->d_high;
   sc.d_low = cfg->d_low;
   sc.causal = cfg->causal;
+  sc.qsq = pa.sq[0];
+  sc.ksq = pa.sq[1];
+  sc.pervec = cfg->tau_mode == PRISM_TAU_PERVEC;
 
   prism::TopPArgs tp;
   tp.logits = sc.logits;

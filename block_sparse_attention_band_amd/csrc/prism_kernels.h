@@ -38,7 +38,7 @@ struct TauArgs {
   int32_t hq, hkv, nb;
   int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
   int32_t d_high, d_low, overlap;
-  int32_t tau_none;
+  int32_t tau_mode;        // prism_tau_mode_t
 };
 
 // Band logits in the workspace: one fp32 plane per (batch, query head,
@@ -63,6 +63,8 @@ struct ScoreArgs {
   int32_t seg_lo, seg_hi, overlap;
   int32_t d_high, d_low;
   int32_t causal;
+  const float *qsq, *ksq;  // per-block segment energies (per-vector temperature)
+  int32_t pervec;          // 1: scale logits by the per-vector band factors
 };
 
 struct TopPArgs {

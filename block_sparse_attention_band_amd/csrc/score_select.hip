@@ -519,7 +519,17 @@ __device__ __forceinline__ void score_tile(const float4 (&qa)[16], const float4 
 // global loads in flight while the current one is computed. LDS rows are 512
 // bytes; 16-byte slot s of row r sits at s ^ (r % 16), so the 16 rows one
 // ds_read_b128 pass touches fall in 16 different bank groups.
-template <int LO8, int HI8>
+// Per-vector temperature factor r_z(v) = R(v, D_full) / R(v, D_z) of one
+// pooled vector from its segment energies e = (high-only, middle, low-only);
+// 1 when the band holds no energy.
+__device__ __forceinline__ float pervec_factor(const float4 &e, int z, int overlap, int dz) {
+  const float mid = overlap ? e.y : 0.f;
+  const float ez = (z == 0 ? e.x : e.z) + mid;
+  const float ef = e.x + e.y + e.z;
+  return ez > 0.f ? sqrtf(ef * (float)dz / ((float)kHeadDim * ez)) : 1.f;
+}
+
+template <int LO8, int HI8, bool PV>
 __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) float4 kt[2][64 * 32];
   const int nI = (a.nb + 63) / 64;
@@ -612,6 +622,13 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
       for (int r = 0; r < 16; ++r) { acc0[r] = 0.f; acc1[r] = 0.f; acc2[r] = 0.f; }
       score_tile<LO8, HI8>(qa, kt[cur] + krow * 32, krow, hf, lo, hi, a.overlap, acc0, acc1, acc2);
       const int j = j0 + r32;
+      float kfh = 1.f, kfl = 1.f;  // per-vector factors of key block j
+      if constexpr (PV) {
+        const float4 e = *reinterpret_cast<const float4 *>(a.ksq + (((int64_t)b * a.hkv + g) * a.nb +
+                                                                    min(j, a.nb - 1)) * 4);
+        kfh = pervec_factor(e, 0, a.overlap, a.d_high);
+        kfl = pervec_factor(e, 1, a.overlap, a.d_low);
+      }
       // acc[r] = segment dot of query block i0 + 8(r/4) + 4*hf + r%4 with
       // key block j; each group of 4 rows starts at a multiple of 4, so the
       // 4 row starts are base + rr * step (32-bit offsets within the plane)
@@ -627,8 +644,14 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
           if (i < a.nb && j < a.nb && (!a.causal || j <= i)) {
             const float mid = a.overlap ? acc1[r] : 0.f;
             const int o = base + rr * step + j;
-            ph[o] = (acc0[r] + mid) * ch;
-            pl[o] = (acc2[r] + mid) * cl;
+            if constexpr (PV) {
+              const float4 e = *reinterpret_cast<const float4 *>(a.qsq + ((int64_t)bh * a.nb + i) * 4);
+              ph[o] = (acc0[r] + mid) * ch * (pervec_factor(e, 0, a.overlap, a.d_high) * kfh);
+              pl[o] = (acc2[r] + mid) * cl * (pervec_factor(e, 1, a.overlap, a.d_low) * kfl);
+            } else {
+              ph[o] = (acc0[r] + mid) * ch;
+              pl[o] = (acc2[r] + mid) * cl;
+            }
           }
         }
       }
@@ -718,10 +741,17 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   int per_head = 0;
   for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
   const dim3 grid(per_head * a.nh * a.batch);  // heads x (full chunks, then remainders)
-  if (a.seg_lo == 32 && a.seg_hi == 64) hipLaunchKernelGGL((score_kernel<4, 8>), grid, dim3(256), 0, s, a);
-  else if (a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0 && a.seg_lo == 0 && a.seg_hi == 128)
-    hipLaunchKernelGGL((score_kernel<0, 16>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((score_kernel<-1, -1>), grid, dim3(256), 0, s, a);
+  const bool def = a.seg_lo == 32 && a.seg_hi == 64, equal = a.seg_lo == 0 && a.seg_hi == 128;
+  if (a.pervec) {
+    if (def) hipLaunchKernelGGL((score_kernel<4, 8, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((score_kernel<-1, -1, true>), grid, dim3(256), 0, s, a);
+  } else if (def) {
+    hipLaunchKernelGGL((score_kernel<4, 8, false>), grid, dim3(256), 0, s, a);
+  } else if (equal) {
+    hipLaunchKernelGGL((score_kernel<0, 16, false>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((score_kernel<-1, -1, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -69,8 +69,19 @@ typedef enum { PRISM_ROPE_INTERLEAVED = 0, PRISM_ROPE_HALF = 1 } prism_rope_layo
 /* FULLSPEC: tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full)),
  *           R = RMS over all pooled blocks of the head and the band's dims;
  *           tau_z = 1 when any R is 0.
- * NONE:     tau_z = 1 (plain pooled scores per band). */
-typedef enum { PRISM_TAU_FULLSPEC = 0, PRISM_TAU_NONE = 1 } prism_tau_mode_t;
+ * NONE:     tau_z = 1 (plain pooled scores per band).
+ * UNIT:     tau_z = R(Qbar,D_z) R(Kbar,D_z) (unit-energy reading; 1 when any R is 0).
+ * PERVEC:   tau_z = 1, and the logit of query block i and key block j is scaled by
+ *           r_z(Qbar_i) r_z(Kbar_j) with r_z(v) = R(v,D_full) / R(v,D_z) taken over
+ *           that one pooled vector (1 when R(v,D_z) is 0).
+ * UNIT and PERVEC are the two readings of the (unprinted) temperature formula
+ * that FULLSPEC was chosen over; they exist for comparison. */
+typedef enum {
+  PRISM_TAU_FULLSPEC = 0,
+  PRISM_TAU_NONE = 1,
+  PRISM_TAU_UNIT = 2,
+  PRISM_TAU_PERVEC = 3
+} prism_tau_mode_t;
 
 typedef struct {
   void *data;        /* device address of element [0, 0, 0, 0] */

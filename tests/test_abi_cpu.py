@@ -113,6 +113,9 @@ def test_workspace_layout(lib):
                                         ctypes.byref(L))
     assert (L.seg_lo, L.seg_hi, L.overlap) == (32, 80, 0)
     assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(p=1.5))) == 0
+    for mode in (1, 2, 3):  # NONE, UNIT, PERVEC are valid temperature modes; 4 is not
+        assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(tau_mode=mode))) > 0
+    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(tau_mode=4))) == 0
 
 
 E = _abi

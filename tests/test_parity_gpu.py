@@ -81,6 +81,10 @@ SMALL = {
     "p_half": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(p=0.5), "bshd", "interleaved"),
     "p_one": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(p=1.0), "bshd", "interleaved"),
     "tau_none": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(tau_mode="none"), "bshd", "interleaved"),
+    "tau_unit": ("llama3_8b_32k", dict(seq=3000, hq=4, hkv=2), dict(tau_mode="unit"), "bshd", "interleaved"),
+    "tau_pervec": ("llama3_8b_32k", dict(seq=3000, hq=4, hkv=2), dict(tau_mode="pervec"), "bshd", "interleaved"),
+    "tau_pervec_gap": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(tau_mode="pervec", d_high=32, d_low=48),
+                       "bshd", "interleaved"),
     "one_block": ("llama3_8b_32k", dict(seq=100, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "fp32_iid": ("tiny_fp32_2k", dict(seq=1900, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128 - 5, hq=1, hkv=1), {}, "bshd", "interleaved"),
