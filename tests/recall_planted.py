@@ -14,8 +14,11 @@ softmax mass on the keys of block j. For a block mask M the script reports
                  token n = 0 mod 4096 (vertical),
 for Prism (d_high=64, d_low=96, RMS-energy temperature), Prism without the
 temperature, and plain mean pooling (one full band, no temperature) at the
-same p and at the p that matches Prism's density. The estimators are the
-CPU oracle's; the GPU path produces the same masks up to counted ties.
+same p and at the p that matches Prism's density. With --equal-recall it also
+runs the two rejected temperature readings (unit-energy, per-vector RMS) and
+reports, for every estimator, the density it needs to reach the mass recall
+Prism has at the pages' p. The estimators are the CPU oracle's; the GPU path
+produces the same masks up to counted ties.
 """
 from __future__ import annotations
 
@@ -86,10 +89,26 @@ def metrics(M, A, P):
 
 PRISM = dict(d_high=64, d_low=96, tau_mode="fullspec")
 PRISM_NO_TAU = dict(d_high=64, d_low=96, tau_mode="none")
+PRISM_UNIT = dict(d_high=64, d_low=96, tau_mode="unit")
+PRISM_PERVEC = dict(d_high=64, d_low=96, tau_mode="pervec")
 PLAIN = dict(d_high=128, d_low=128, tau_mode="none")
+ESTIMATORS = {"prism": PRISM, "prism_no_tau": PRISM_NO_TAU, "prism_unit_tau": PRISM_UNIT,
+              "prism_pervec_tau": PRISM_PERVEC, "plain": PLAIN}
 
 
-def run(seq=16384, heads=4, verbose=True):
+def p_for(target, metric_ix, q64, k64, A, P, block, kw, lo=0.3, hi=0.99999, iters=16):
+    """Smallest p (bisection) at which metric `metric_ix` (0 density, 1 mass
+    recall) of the estimator reaches `target`; returns (p, metrics)."""
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if metrics(masks(q64, k64, block, mid, **kw), A, P)[metric_ix] < target:
+            lo = mid
+        else:
+            hi = mid
+    return hi, metrics(masks(q64, k64, block, hi, **kw), A, P)
+
+
+def run(seq=16384, heads=4, verbose=True, equal_recall=False):
     w = WORKLOADS["qwen3_8b_64k"].scaled(seq=seq, hq=heads, hkv=1)
     q, k, _ = make_qkv(w, with_v=False)
     q64, k64 = to_f64(q, "bf16")[0], to_f64(k, "bf16")[0]
@@ -99,26 +118,34 @@ def run(seq=16384, heads=4, verbose=True):
     rows["prism"] = (w.p,) + metrics(masks(q64, k64, w.block, w.p, **PRISM), A, P)
     rows["prism_no_tau"] = (w.p,) + metrics(masks(q64, k64, w.block, w.p, **PRISM_NO_TAU), A, P)
     rows["plain_same_p"] = (w.p,) + metrics(masks(q64, k64, w.block, w.p, **PLAIN), A, P)
-    target = rows["prism"][1]
-    lo, hi = 0.5, 0.9999
-    for _ in range(14):
-        mid = 0.5 * (lo + hi)
-        if metrics(masks(q64, k64, w.block, mid, **PLAIN), A, P)[0] < target:
-            lo = mid
-        else:
-            hi = mid
-    rows["plain_density_matched"] = (hi,) + metrics(masks(q64, k64, w.block, hi, **PLAIN), A, P)
+    pm, m = p_for(rows["prism"][1], 0, q64, k64, A, P, w.block, PLAIN, lo=0.5, hi=0.9999, iters=14)
+    rows["plain_density_matched"] = (pm,) + m
+    recall = {}
+    if equal_recall:
+        # the temperature readings side by side: density each needs to reach
+        # the mass recall Prism (adopted reading) has at the pages' p
+        rows["prism_unit_tau"] = (w.p,) + metrics(masks(q64, k64, w.block, w.p, **PRISM_UNIT), A, P)
+        rows["prism_pervec_tau"] = (w.p,) + metrics(masks(q64, k64, w.block, w.p, **PRISM_PERVEC), A, P)
+        target = rows["prism"][2]
+        for name, kw in ESTIMATORS.items():
+            recall[name] = (target,) + p_for(target, 1, q64, k64, A, P, w.block, kw)
     if verbose:
         print(f"qwen3-shaped planted workload: seq={seq} heads={heads} (1 KV head), B=128")
         print(f"{'estimator':24s} {'p':>7s} {'density':>8s} {'mass recall':>12s} {'planted recall':>15s}")
         for name, (p, d, m, pr) in rows.items():
             print(f"{name:24s} {p:7.4f} {d:8.4f} {m:12.5f} {pr:15.4f}")
-    return rows, A, P
+        if recall:
+            print(f"at equal mass recall {next(iter(recall.values()))[0]:.5f}:")
+            for name, (t, p, (d, m, pr)) in recall.items():
+                print(f"{name:24s} {p:7.4f} {d:8.4f} {m:12.5f} {pr:15.4f}")
+    return rows, A, P, recall
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--seq", type=int, default=16384)
     ap.add_argument("--heads", type=int, default=4)
+    ap.add_argument("--equal-recall", action="store_true",
+                    help="also compare the temperature readings at equal mass recall")
     a = ap.parse_args()
-    run(a.seq, a.heads)
+    run(a.seq, a.heads, equal_recall=a.equal_recall)

@@ -21,8 +21,11 @@ def test_block_mass_rows_sum_to_one_and_full_mask_recalls_all():
 
 
 def test_recall_comparison_small():
-    rows, A, P = run(seq=4096, heads=2, verbose=True)
+    rows, A, P, recall = run(seq=4096, heads=2, verbose=True, equal_recall=True)
     for name, (p, d, m, pr) in rows.items():
         assert 0 < d <= 1 and 0 < m <= 1 and 0 < pr <= 1, name
     # density matching hits Prism's density within one block row's worth
     assert abs(rows["plain_density_matched"][1] - rows["prism"][1]) < 0.02
+    # equal-recall search reaches the target mass recall for every reading
+    for name, (target, p, (d, m, pr)) in recall.items():
+        assert m >= target - 1e-9 and 0 < d <= 1, name
