@@ -13,6 +13,26 @@ The Prism pages name RoPE as the source of the high/low frequency split
 Technical Summary, section 1) but print no formula, so the RoFormer form is
 used. Angles are computed in float64.
 
+The pages also state that the method carries over to YaRN and M-RoPE
+(gist.science, Results, generalization). Both are generated here from
+their published definitions (class Rope): the estimator is unchanged, only
+the angles differ.
+  YaRN ("NTK-by-parts", Peng et al. 2023): with the original context L0,
+    the scale s and r_j = L0 theta_j / (2 pi) (how many turns pair j makes
+    over L0), gamma_j = clip((r_j - beta_slow) / (beta_fast - beta_slow),
+    0, 1) and theta'_j = gamma_j theta_j + (1 - gamma_j) theta_j / s: fast
+    pairs keep their frequency, slow pairs are interpolated. Q and K are
+    both multiplied by the attention factor 0.1 ln(s) + 1.
+  M-RoPE (Qwen2-VL; Qwen3-VL's interleaved variant): every token has three
+    position ids (t, h, w) and pair j rotates by the id of its axis. Text
+    tokens have t = h = w = their running position. A video prefix of
+    nt x nh x nw patch tokens (frame-major, then row, then column) has ids
+    (frame, row, column); text after it continues from max(nt, nh, nw).
+    'sectioned' gives the first sections[0] pairs to t, the next
+    sections[1] to h, the rest to w; 'interleaved' gives pair j to h when
+    j = 1 mod 3 and j < 3 sections[1], to w when j = 2 mod 3 and
+    j < 3 sections[2], and to t otherwise.
+
 Every value is generated in float32, rotated in float64, rounded to float32
 (round-to-nearest-even) and then, for bf16 workloads, to bfloat16
 (round-to-nearest-even). The same bytes go to the GPU and to the oracle.
@@ -30,6 +50,21 @@ import numpy as np
 
 # tensor ids for seeding
 T_QNOISE, T_KNOISE, T_V, T_SEMANTIC, T_SLASH = 0, 1, 2, 3, 4
+
+
+@dataclass(frozen=True)
+class Rope:
+    """Which rotary embedding makes the post-RoPE inputs (see the module
+    docstring for the formulas)."""
+
+    kind: str = "default"  # "default", "yarn", "mrope"
+    factor: float = 1.0  # YaRN scale s
+    orig_ctx: int = 0  # YaRN original context L0
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+    mrope: str = "sectioned"  # or "interleaved"
+    sections: tuple = ()  # pairs per axis (t, h, w), summing to d/2
+    grid: tuple = (0, 0, 0)  # video prefix (frames, rows, columns) in patch tokens
 
 
 @dataclass(frozen=True)
@@ -52,6 +87,7 @@ class Workload:
     d_high: int = 64
     d_low: int = 96
     causal: bool = True
+    rope: Rope = Rope()
 
     @property
     def nb(self) -> int:
@@ -72,6 +108,15 @@ WORKLOADS = {
     "llama3_8b_128k": Workload("llama3_8b_128k", 3, 1, 131072, 32, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
     "qwen3_8b_64k": Workload("qwen3_8b_64k", 4, 1, 65536, 32, 8, 128, "bf16", 1e6, "semantic", True, 0.93),
     "llama3_70b_share_128k": Workload("llama3_70b_share_128k", 5, 1, 131072, 64, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
+    # RoPE variants the pages say the method carries over to: Qwen3-8B
+    # extended from 32K to 128K by YaRN (factor 4), and a Qwen3-VL-8B-shaped
+    # layer (interleaved M-RoPE, sections 24/20/20, base 5e6) over a video of
+    # 16 frames x 32 x 48 patch tokens followed by text.
+    "qwen3_8b_yarn_128k": Workload("qwen3_8b_yarn_128k", 6, 1, 131072, 32, 8, 128, "bf16", 1e6, "semantic", False,
+                                   0.93, rope=Rope("yarn", factor=4.0, orig_ctx=32768)),
+    "qwen3_vl_8b_video_32k": Workload("qwen3_vl_8b_video_32k", 7, 1, 32768, 32, 8, 128, "bf16", 5e6, "semantic", False,
+                                      0.93, rope=Rope("mrope", mrope="interleaved", sections=(24, 20, 20),
+                                                      grid=(16, 32, 48))),
 }
 
 
@@ -79,12 +124,54 @@ def _rng(seed: int, tensor_id: int, head: int, batch: int) -> np.random.Generato
     return np.random.default_rng([seed, tensor_id, head, batch])
 
 
-def rope_tables(seq: int, d: int, theta: float) -> tuple[np.ndarray, np.ndarray]:
-    """cos/sin of t*theta_j for t < seq, j < d/2, in float64."""
+def rope_freqs(d: int, theta: float, rope: Rope = Rope()) -> np.ndarray:
+    """theta_j (rad per position) of pairs j < d/2, YaRN-rescaled if asked."""
     j = np.arange(d // 2, dtype=np.float64)
     freq = theta ** (-2.0 * j / d)
-    ang = np.arange(seq, dtype=np.float64)[:, None] * freq[None, :]
-    return np.cos(ang), np.sin(ang)
+    if rope.kind == "yarn":
+        r = rope.orig_ctx * freq / (2.0 * np.pi)
+        gamma = np.clip((r - rope.beta_slow) / (rope.beta_fast - rope.beta_slow), 0.0, 1.0)
+        freq = gamma * freq + (1.0 - gamma) * freq / rope.factor
+    return freq
+
+
+def rope_positions(seq: int, rope: Rope = Rope()) -> np.ndarray:
+    """Position ids [seq, 3] (t, h, w); equal columns unless M-RoPE."""
+    n = np.arange(seq, dtype=np.int64)
+    pos = np.repeat(n[:, None], 3, axis=1)
+    if rope.kind == "mrope":
+        nt, nh, nw = rope.grid
+        nv = min(seq, nt * nh * nw)
+        v = n[:nv]
+        pos[:nv] = np.stack([v // (nh * nw), (v // nw) % nh, v % nw], axis=1)
+        if seq > nv:
+            pos[nv:] = (max(nt, nh, nw) + n[nv:] - nv)[:, None]
+    return pos
+
+
+def rope_axes(d: int, rope: Rope = Rope()) -> np.ndarray:
+    """Axis (0 t, 1 h, 2 w) whose position id turns pair j."""
+    j = np.arange(d // 2)
+    if rope.kind != "mrope":
+        return np.zeros(d // 2, np.int64)
+    st, sh, sw = rope.sections
+    if st + sh + sw != d // 2:
+        raise ValueError("M-RoPE sections must sum to d/2")
+    if rope.mrope == "sectioned":
+        return np.where(j < st, 0, np.where(j < st + sh, 1, 2))
+    if rope.mrope == "interleaved":
+        return np.where((j % 3 == 1) & (j < 3 * sh), 1, np.where((j % 3 == 2) & (j < 3 * sw), 2, 0))
+    raise ValueError(rope.mrope)
+
+
+def rope_tables(seq: int, d: int, theta: float, rope: Rope = Rope()) -> tuple[np.ndarray, np.ndarray]:
+    """cos/sin [seq, d/2] of the angle of pair j at token t, in float64 (for
+    YaRN times the attention factor 0.1 ln(s) + 1)."""
+    freq = rope_freqs(d, theta, rope)
+    pos = rope_positions(seq, rope).astype(np.float64)
+    ang = pos[:, rope_axes(d, rope)] * freq[None, :]
+    amp = 0.1 * np.log(rope.factor) + 1.0 if rope.kind == "yarn" else 1.0
+    return amp * np.cos(ang), amp * np.sin(ang)
 
 
 def apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, layout: str) -> np.ndarray:
@@ -150,7 +237,7 @@ def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True)
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
-    cos, sin = rope_tables(N, d, w.theta)
+    cos, sin = rope_tables(N, d, w.theta, w.rope)
     st = np.uint16 if w.dtype == "bf16" else np.float32
     q = np.empty((b, N, Hq, d), st)
     k = np.empty((b, N, Hkv, d), st)
@@ -218,6 +305,6 @@ def planted_blocks(w: Workload) -> dict:
 
 
 __all__ = [
-    "Workload", "WORKLOADS", "make_qkv", "rope_tables", "apply_rope", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "to_f64", "random_mask", "planted_blocks",
+    "Rope", "Workload", "WORKLOADS", "make_qkv", "rope_freqs", "rope_positions", "rope_axes", "rope_tables",
+    "apply_rope", "f32_to_bf16_bits", "bf16_bits_to_f32", "to_f64", "random_mask", "planted_blocks",
 ]

@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 
 import block_sparse_attention_band_amd as prism  # noqa: E402
 import oracle.prism_oracle as po  # noqa: E402
-from synth import WORKLOADS, make_qkv, random_mask, to_f64  # noqa: E402
+from synth import WORKLOADS, Rope, make_qkv, random_mask, to_f64  # noqa: E402
 from tests.parity import compare_masks, logit_row, oracle_estimate_heads, to_device  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -88,6 +88,11 @@ SMALL = {
     "one_block": ("llama3_8b_32k", dict(seq=100, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "fp32_iid": ("tiny_fp32_2k", dict(seq=1900, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128 - 5, hq=1, hkv=1), {}, "bshd", "interleaved"),
+    # RoPE variants (inputs only; the estimator is the same)
+    "yarn": ("qwen3_8b_yarn_128k", dict(seq=5000, hq=4, hkv=1), {}, "bshd", "interleaved"),
+    "mrope_video": ("qwen3_vl_8b_video_32k",
+                    dict(seq=6000, hq=4, hkv=1, rope=Rope("mrope", mrope="interleaved", sections=(24, 20, 20),
+                                                          grid=(2, 16, 48))), {}, "bshd", "interleaved"),
 }
 
 
