@@ -17,8 +17,10 @@ temperature, and plain mean pooling (one full band, no temperature) at the
 same p and at the p that matches Prism's density. With --equal-recall it also
 runs the two rejected temperature readings (unit-energy, per-vector RMS) and
 reports, for every estimator, the density it needs to reach the mass recall
-Prism has at the pages' p. The estimators are the CPU oracle's; the GPU path
-produces the same masks up to counted ties.
+Prism has at the pages' p. --split-sweep does the same over a sweep of band
+splits (d_high, d_low) with the adopted temperature. The estimators are the CPU
+oracle's; the GPU path produces the same masks up to counted ties (it takes
+any even band widths).
 """
 from __future__ import annotations
 
@@ -141,11 +143,36 @@ def run(seq=16384, heads=4, verbose=True, equal_recall=False):
     return rows, A, P, recall
 
 
+def split_sweep(seq=16384, heads=4, splits=((32, 96), (48, 96), (64, 96), (80, 96), (96, 96), (64, 64),
+                                          (64, 80), (64, 112), (64, 128), (32, 112), (96, 64)), verbose=True):
+    """Band-split ablation: for each (d_high, d_low), the density Prism needs
+    to reach the mass recall the pages' split (64, 96) has at the pages' p."""
+    w = WORKLOADS["qwen3_8b_64k"].scaled(seq=seq, hq=heads, hkv=1)
+    q, k, _ = make_qkv(w, with_v=False)
+    q64, k64 = to_f64(q, "bf16")[0], to_f64(k, "bf16")[0]
+    A = block_attention_mass(q64, k64, w.block)
+    P = planted_blocks(w.seq, w.block)
+    target = metrics(masks(q64, k64, w.block, w.p, **PRISM), A, P)[1]
+    out = {}
+    for dh, dl in splits:
+        kw = dict(d_high=dh, d_low=dl, tau_mode="fullspec")
+        out[(dh, dl)] = p_for(target, 1, q64, k64, A, P, w.block, kw)
+        if verbose:
+            p, (d, m, pr) = out[(dh, dl)]
+            print(f"d_high={dh:3d} d_low={dl:3d}  p={p:.4f} density={d:.4f} mass={m:.5f} planted={pr:.4f}", flush=True)
+    return target, out
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--seq", type=int, default=16384)
     ap.add_argument("--heads", type=int, default=4)
     ap.add_argument("--equal-recall", action="store_true",
                     help="also compare the temperature readings at equal mass recall")
+    ap.add_argument("--split-sweep", action="store_true",
+                    help="density at equal mass recall over a sweep of band splits")
     a = ap.parse_args()
-    run(a.seq, a.heads, equal_recall=a.equal_recall)
+    if a.split_sweep:
+        split_sweep(a.seq, a.heads)
+    else:
+        run(a.seq, a.heads, equal_recall=a.equal_recall)

@@ -2,7 +2,7 @@
 its metric behaves as defined, and its comparison runs end to end."""
 import numpy as np
 
-from tests.recall_planted import block_attention_mass, masks, metrics, planted_blocks, run
+from tests.recall_planted import block_attention_mass, masks, metrics, planted_blocks, run, split_sweep
 
 
 def test_block_mass_rows_sum_to_one_and_full_mask_recalls_all():
@@ -29,3 +29,11 @@ def test_recall_comparison_small():
     # equal-recall search reaches the target mass recall for every reading
     for name, (target, p, (d, m, pr)) in recall.items():
         assert m >= target - 1e-9 and 0 < d <= 1, name
+
+
+def test_split_sweep_small():
+    target, out = split_sweep(seq=4096, heads=2, splits=((64, 96), (32, 112)), verbose=True)
+    # the pages' split at its own p reaches the target at p <= the pages' p
+    assert out[(64, 96)][0] <= 0.93 + 1e-9
+    for (dh, dl), (p, (d, m, pr)) in out.items():
+        assert m >= target - 1e-9 and 0 < d <= 1, (dh, dl)
