@@ -6,7 +6,9 @@ This module only marshals arguments: it turns torch tensors (device memory on
 the current HIP stream) into the ABI's plain descriptors and calls the
 library. Every step of the path runs in the library's kernels; there is no
 fallback. Tensors are [batch, seq, heads, 128] with the last dim contiguous
-(any batch/seq/head strides), bf16 or fp32.
+(any batch/seq/head strides), bf16 or fp32. Block masks are either uint8
+[batch, heads, nb, nb] (one byte per block) or bit-packed int32
+[batch, heads, nb, ceil(nb / 32)] (bit j % 32 of word j / 32 = key block j).
 """
 from __future__ import annotations
 
@@ -63,11 +65,17 @@ def tensor_desc(t) -> PrismTensor:
 
 
 def mask_desc(m, block_size: int, causal: bool) -> PrismMask:
+    """Descriptor of a block mask: uint8 [b, H, nb, nb], or int32 [b, H, nb, ceil(nb/32)] bit-packed."""
     torch = _torch()
-    if m.dtype != torch.uint8 or m.dim() != 4 or not m.is_contiguous():
-        raise ValueError("mask must be a contiguous uint8 [batch, heads, nb, nb] tensor")
-    b, h, nq, nk = m.shape
-    return PrismMask(m.data_ptr(), b, h, nq, nk, block_size, int(bool(causal)))
+    if m.dim() != 4 or not m.is_contiguous() or m.dtype not in (torch.uint8, torch.int32):
+        raise ValueError("mask must be a contiguous uint8 [batch, heads, nb, nb] or int32 "
+                         "[batch, heads, nb, ceil(nb/32)] tensor")
+    b, h, nq, w = m.shape
+    if m.dtype == torch.uint8:
+        return PrismMask(m.data_ptr(), b, h, nq, w, block_size, int(bool(causal)), _abi.MASK_U8, 0)
+    if w != (nq + 31) // 32:
+        raise ValueError("a bit-packed mask row holds ceil(nb / 32) int32 words")
+    return PrismMask(m.data_ptr(), b, h, nq, nq, block_size, int(bool(causal)), _abi.MASK_BITS, 0)
 
 
 def _cfg(cfg: EstimatorConfig, workspace=None) -> PrismCfg:
@@ -101,14 +109,19 @@ def new_workspace(q, k, cfg: EstimatorConfig = EstimatorConfig()):
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
-def estimate(q, k, cfg: EstimatorConfig = EstimatorConfig(), *, workspace=None, mask_out=None):
-    """Prism's block mask M [batch, Hq, nb, nb] (uint8, 1 = compute) for post-RoPE q, k."""
+def estimate(q, k, cfg: EstimatorConfig = EstimatorConfig(), *, workspace=None, mask_out=None, bits: bool = False):
+    """Prism's block mask M for post-RoPE q, k: uint8 [batch, Hq, nb, nb] (1 = compute), or with
+    bits=True (or an int32 mask_out) bit-packed int32 [batch, Hq, nb, ceil(nb / 32)]."""
     torch = _torch()
     L = workspace_layout(q, k, cfg)
     if workspace is None:
         workspace = torch.empty(L.total_bytes, dtype=torch.uint8, device=q.device)
     if mask_out is None:
-        mask_out = torch.empty((q.shape[0], q.shape[2], L.nb, L.nb), dtype=torch.uint8, device=q.device)
+        if bits:
+            mask_out = torch.empty((q.shape[0], q.shape[2], L.nb, (L.nb + 31) // 32), dtype=torch.int32,
+                                   device=q.device)
+        else:
+            mask_out = torch.empty((q.shape[0], q.shape[2], L.nb, L.nb), dtype=torch.uint8, device=q.device)
     qd, kd, c = tensor_desc(q), tensor_desc(k), _cfg(cfg, workspace)
     md = mask_desc(mask_out, cfg.block_size, cfg.causal)
     _abi.check(lib().prism_estimate(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(c), ctypes.byref(md),

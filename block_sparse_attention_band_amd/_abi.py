@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 2
+PRISM_ABI_VERSION = 3
 
 # prism_status_t
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH = range(10)
@@ -22,6 +22,7 @@ STATUS_NAMES = ["PRISM_OK", "PRISM_ERR_NULL", "PRISM_ERR_DTYPE", "PRISM_ERR_SHAP
 BF16, FP32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 TAU_FULLSPEC, TAU_NONE, TAU_UNIT, TAU_PERVEC = 0, 1, 2, 3
+MASK_U8, MASK_BITS = 0, 1
 
 
 class PrismTensor(ctypes.Structure):
@@ -37,6 +38,7 @@ class PrismMask(ctypes.Structure):
         ("data", ctypes.c_void_p), ("batch", ctypes.c_int64), ("heads", ctypes.c_int64),
         ("nq_blocks", ctypes.c_int64), ("nk_blocks", ctypes.c_int64),
         ("block_size", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("format", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 

@@ -92,6 +92,13 @@ void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_c
   L->reserved = 0;
 }
 
+// format and alignment of a mask descriptor; 0 or a status
+int check_mask_format(const prism_mask_t *m) {
+  if (m->format != PRISM_MASK_U8 && m->format != PRISM_MASK_BITS) return PRISM_ERR_CONFIG;
+  if (reinterpret_cast<uintptr_t>(m->data) % (m->format == PRISM_MASK_U8 ? 16 : 4)) return PRISM_ERR_ALIGN;
+  return PRISM_OK;
+}
+
 prism::TensorArg targ(const prism_tensor_t *t) {
   prism::TensorArg a;
   a.data = t->data;
@@ -155,7 +162,7 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   if (mask_out->batch != q->batch || mask_out->heads != q->heads || mask_out->nq_blocks != L.nb ||
       mask_out->nk_blocks != L.nb || mask_out->block_size != cfg->block_size)
     return PRISM_ERR_SHAPE;
-  if (reinterpret_cast<uintptr_t>(mask_out->data) % 16) return PRISM_ERR_ALIGN;
+  if ((st = check_mask_format(mask_out))) return st;
 
   char *ws = static_cast<char *>(cfg->workspace);
   const int fp32 = q->dtype == PRISM_FP32;
@@ -211,6 +218,8 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   prism::TopPArgs tp;
   tp.logits = sc.logits;
   tp.mask = mask_out->data;
+  tp.bits = mask_out->format == PRISM_MASK_BITS;
+  tp.words = (int)((L.nb + 31) / 32);
   tp.plane = L.logits_plane;
   tp.hq = ta.hq;
   tp.nb = nb;
@@ -258,6 +267,7 @@ int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, co
   if (nb > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
   if (mask->batch != q->batch || mask->heads != q->heads || mask->nq_blocks != nb || mask->nk_blocks != nb)
     return PRISM_ERR_SHAPE;
+  if ((st = check_mask_format(mask))) return st;
 
   prism::AttnArgs a;
   a.q = targ(q);
@@ -265,6 +275,8 @@ int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, co
   a.v = targ(v);
   a.o = targ(out);
   a.mask = mask->data;
+  a.bits = mask->format == PRISM_MASK_BITS;
+  a.words = (int)((nb + 31) / 32);
   a.batch = (int)q->batch;
   a.seq = (int)q->seq;
   a.nb = (int)nb;

@@ -9,7 +9,9 @@ namespace prism {
 
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 128;
-constexpr int kMaxBlocks = 2048;
+constexpr int kMaxBlocks = 8192;   // blocks per sequence (1,048,576 tokens)
+constexpr int kShortRow = 2048;    // rows up to this many blocks: register-resident selection
+constexpr int kListCap = 2048;     // attention: key blocks compacted per pass over a mask row
 
 // One tensor [batch, seq, heads, 128], strides in elements.
 struct TensorArg {
@@ -69,7 +71,9 @@ struct ScoreArgs {
 
 struct TopPArgs {
   const float *logits;
-  uint8_t *mask;           // [batch][Hq][nb][nb]
+  void *mask;              // [batch][Hq][nb][row]: nb bytes, or `words` u32 of bits
+  int32_t bits;            // 1: bit-packed rows
+  int32_t words;           // u32 words per bit-packed row, ceil(nb / 32)
   int64_t plane;
   int32_t hq, nb, batch;
   int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
@@ -85,7 +89,9 @@ hipError_t launch_topp(const TopPArgs &a, hipStream_t s);
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   TensorArg q, k, v, o;
-  const uint8_t *mask;     // [batch][Hq][nb][nb]
+  const void *mask;        // [batch][Hq][nb][row]: nb bytes, or `words` u32 of bits
+  int32_t bits;            // 1: bit-packed rows
+  int32_t words;
   int32_t batch, seq, nb, hq, hkv;
   int32_t causal;
   float scale_log2;        // log2(e) / sqrt(head_dim)

@@ -95,8 +95,10 @@ __device__ __forceinline__ uint32_t scan_keep(uint32_t x, Op op) {
 
 __device__ __forceinline__ uint32_t lane63(uint32_t v) { return __builtin_amdgcn_readlane(v, 63); }
 __device__ __forceinline__ unsigned long long lane63(unsigned long long v) {
-  return ((unsigned long long)__builtin_amdgcn_readlane((uint32_t)(v >> 32), 63) << 32) |
-         __builtin_amdgcn_readlane((uint32_t)v, 63);
+  // readlane returns int: widen each half as unsigned (no sign extension)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -663,6 +665,42 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
 #undef PRISM_STORE_TILE
 }
 
+// Writes one chunk of a mask row from the wave's selection bits: bit
+// 4 e4 + m of lane l is block jbase + 4 l + 256 e4 + m, for e4 < ne4 (every
+// block of the chunk below nb is written, zeros included). U8 rows get one
+// byte per block; bit-packed rows one u32 per 32 blocks, which are the
+// nibbles of 8 adjacent lanes (gathered by lane exchanges, all lanes taking
+// part).
+__device__ void write_mask_chunk(const TopPArgs &a, int64_t row_index, int jbase, int ne4, uint32_t bits, int lane) {
+  if (a.bits) {
+    uint32_t *wrow = static_cast<uint32_t *>(a.mask) + row_index * a.words;
+    for (int e4 = 0; e4 < ne4; ++e4) {
+      uint32_t v = ((bits >> (4 * e4)) & 0xFu) << (4 * (lane & 7));
+      v |= __shfl_xor(v, 1);
+      v |= __shfl_xor(v, 2);
+      v |= __shfl_xor(v, 4);
+      const int j = jbase + 256 * e4 + 32 * (lane >> 3);  // first block of the word
+      if ((lane & 7) == 0 && j < a.nb) wrow[j >> 5] = v;
+    }
+    return;
+  }
+  uint8_t *mrow = static_cast<uint8_t *>(a.mask) + row_index * a.nb;
+  for (int e4 = 0; e4 < ne4; ++e4) {
+    const int j = jbase + 4 * lane + 256 * e4;
+    const uint32_t nib = (bits >> (4 * e4)) & 0xFu;
+    if ((a.nb & 3) == 0) {
+      if (j < a.nb) {
+        const uint32_t word = (nib & 1u) | ((nib >> 1) & 1u) << 8 | ((nib >> 2) & 1u) << 16 | ((nib >> 3) & 1u) << 24;
+        *reinterpret_cast<uint32_t *>(mrow + j) = word;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (j + m < a.nb) mrow[j + m] = (uint8_t)((nib >> m) & 1u);
+    }
+  }
+}
+
 // One workgroup = two rows (batch, head, query block) x two branches: wave w
 // selects branch w % 2 of row w / 2; the branch pairs meet in LDS and the
 // even wave writes the union as the mask row. Rows are taken longest first.
@@ -714,24 +752,139 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
   __syncthreads();
   if (!live || z != 0) return;
   bits |= sel_s[wave + 1][lane];
-
   // union of the branches -> mask row, zeros included
-  uint8_t *mrow = a.mask + ((int64_t)bh * a.nb + i) * a.nb;
+  write_mask_chunk(a, (int64_t)bh * a.nb + i, 0, EPL / 4, bits, lane);
+}
+
+// Top-P of a row of more than kShortRow blocks, one wave, the row read from
+// the logit plane in chunks of 2048 blocks (element k of lane l in chunk c
+// is block 2048 c + 4 l + 256 (k / 4) + k % 4). The selection rule is
+// select_row_hist's: masses m = floor(e 2^31) of e = exp2(L - max), target
+// ceil(p Z), the shortest prefix of (e descending, block ascending) whose
+// mass reaches the target. It is found by bisection on the key (the bit
+// pattern of e, monotone in e): T = the largest key with
+// mass(key >= T) >= target; every key above T is kept, and of the entries
+// with key T the first ceil((target - mass(key > T)) / m(T)) in block order.
+// Keys are recomputed from the logits at every pass (about 32 passes over
+// the row, read from L2). sel[c] receives this lane's bits of chunk c.
+constexpr int kLongChunks = kMaxBlocks / 2048;
+
+__device__ void select_row_long(const float *row, int nc, float p, int lane, uint32_t (&sel)[kLongChunks]) {
+  const int nch = (nc + 2047) / 2048;
+  auto key_of = [&](int c, int e4, float (&x)[4]) {
+    const int j = 2048 * c + 4 * lane + 256 * e4;
+    float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
+    x[0] = t.x;
+    x[1] = (j + 1 < nc) ? t.y : -INFINITY;
+    x[2] = (j + 2 < nc) ? t.z : -INFINITY;
+    x[3] = (j + 3 < nc) ? t.w : -INFINITY;
+  };
+  float mx = -INFINITY;
+  _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
 #pragma unroll
-  for (int e4 = 0; e4 < EPL / 4; ++e4) {
-    const int j = 4 * lane + 256 * e4;
-    const uint32_t nib = (bits >> (4 * e4)) & 0xFu;
-    if ((a.nb & 3) == 0) {
-      if (j < a.nb) {
-        const uint32_t word = (nib & 1u) | ((nib >> 1) & 1u) << 8 | ((nib >> 2) & 1u) << 16 | ((nib >> 3) & 1u) << 24;
-        *reinterpret_cast<uint32_t *>(mrow + j) = word;
+    for (int e4 = 0; e4 < 8; ++e4) {
+      float x[4];
+      key_of(c, e4, x);
+      mx = fmaxf(fmaxf(mx, fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
+    }
+  mx = wave_max(mx);
+  // S(t): fixed-point mass of the entries with key >= t (t = 1: all of them;
+  // exp2(-inf) = 0 marks the inadmissible ones)
+  auto mass_from = [&](uint32_t t, bool strict) -> unsigned long long {
+    unsigned long long sl = 0;
+    _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4) {
+        float x[4];
+        key_of(c, e4, x);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
+          if (strict ? k > t : k >= t) sl += fixed_mass(k);
+        }
       }
-    } else {
+    return lane63(scan_add(sl));
+  };
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
+  if (p >= 1.0f) {
+    _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4) {
+        float x[4];
+        key_of(c, e4, x);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sel[c] |= (x[m] != -INFINITY ? 1u : 0u) << (4 * e4 + m);
+      }
+    return;
+  }
+  const unsigned long long Z = mass_from(1u, false);
+  const unsigned long long target = (unsigned long long)ceil((double)Z * (double)p);
+  // invariant: S(lo) >= target > S(hi); every key is <= 1.0f's
+  uint32_t lo = 1u, hi = 0x3F800001u;
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (mass_from(mid, false) >= target) lo = mid; else hi = mid;
+  }
+  const uint32_t T = lo;
+  const unsigned long long above = mass_from(T, true);
+  const unsigned long long mT = fixed_mass(T);  // > 0: S(T) > S(T + 1)
+  const unsigned long long take = (target - above + mT - 1) / mT;
+  // keep key > T, and the first `take` entries with key T in block order
+  unsigned long long rank0 = 0;
+  _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+    for (int e4 = 0; e4 < 8; ++e4) {
+      float x[4];
+      key_of(c, e4, x);
+      uint32_t tie = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
+        if (k > T) sel[c] |= 1u << (4 * e4 + m);
+        if (k == T) tie |= 1u << m;
+      }
+      const int cnt = __popc(tie);
+      unsigned long long r = rank0 + (unsigned long long)wave_excl_scan_i(cnt, lane);
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        if (j + m < a.nb) mrow[j + m] = (uint8_t)((nib >> m) & 1u);
+        if ((tie >> m) & 1u) {
+          if (r < take) sel[c] |= 1u << (4 * e4 + m);
+          ++r;
+        }
+      rank0 += (unsigned long long)wave_sum_i(cnt);
     }
-  }
+}
+
+// Rows of more than kShortRow blocks: one workgroup = two rows x two
+// branches as in topp_kernel, each wave running select_row_long.
+__global__ __launch_bounds__(256) void topp_long_kernel(TopPArgs a) {
+  __shared__ uint32_t sel_s[4][kLongChunks][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int z = wave & 1;
+  const int nbh = a.batch * a.nh;
+  const int rid = blockIdx.x * 2 + (wave >> 1);
+  const bool live = rid < nbh * a.nb;
+  const int rr = live ? rid : 0;
+  const int i = a.causal ? a.nb - 1 - rr / nbh : rr / nbh;
+  const int lbh = rr % nbh;
+  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+  const int nc = a.causal ? i + 1 : a.nb;
+  const float *row = a.logits + ((int64_t)bh * 2 + z) * a.plane + logit_row(i, a.nb, a.causal);
+  uint32_t sel[kLongChunks];
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
+  if (live) select_row_long(row, nc, a.p, lane, sel);
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c) sel_s[wave][c][lane] = sel[c];
+  __syncthreads();
+  if (!live || z != 0) return;
+  const int nchunks = (a.nb + 2047) / 2048;  // the whole row, zeros included
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c)
+    if (c < nchunks) write_mask_chunk(a, (int64_t)bh * a.nb + i, 2048 * c, 8, sel[c] | sel_s[wave + 1][c][lane], lane);
 }
 
 }  // namespace
@@ -759,7 +912,8 @@ hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {
   const int rows = a.batch * a.nh * a.nb;
   const dim3 grid((rows + 1) / 2);
   if (a.nb <= 1024) hipLaunchKernelGGL((topp_kernel<16>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
+  else if (a.nb <= kShortRow) hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(topp_long_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 //
 // bf16 kernel (gfx950 MFMA), one workgroup of 4 waves per (batch, head,
 // query block of 128 tokens); each wave owns 32 query rows.
-//   * The workgroup compacts its mask row into an ascending list of key
-//     blocks in LDS; only those blocks are loaded and computed.
+//   * The workgroup compacts its mask row (bytes or bits) into an ascending
+//     list of key blocks in LDS, 2048 blocks of the row at a time; only those
+//     blocks are loaded and computed.
 //   * Keys and values stream in sub-tiles of 64 tokens through two LDS
 //     buffers: the next sub-tile's global loads are in flight while the
 //     current one is computed. V is transposed on its way into LDS.
@@ -121,6 +122,24 @@ __device__ __forceinline__ void dma16(const i32x4 &rs, uint8_t *lds, int voff, i
 //    ds_read_b128 pass touches land in 16 different bank groups.
 // V: chunk c of row r sits in slot c ^ (4 * (r & 3)): the 4 rows x 4 chunks
 //    a transposing read touches per half-wave land in 16 different groups.
+// Compacts the selected key blocks jlo..jhi (at most kListCap) of one mask
+// row into blist in ascending order; one wave, lane 0 stores the count.
+__device__ __forceinline__ void compact_row(const AttnArgs &a, int64_t row_index, int jlo, int jhi, int lane,
+                                            int16_t *blist, int *nsel) {
+  const uint8_t *mrow = static_cast<const uint8_t *>(a.mask) + row_index * a.nb;
+  const uint32_t *wrow = static_cast<const uint32_t *>(a.mask) + row_index * a.words;
+  int cnt = 0;
+  for (int j0 = jlo; j0 <= jhi; j0 += 64) {
+    const int j = j0 + lane;
+    bool sel = false;
+    if (j <= jhi) sel = a.bits ? ((wrow[j >> 5] >> (j & 31)) & 1u) != 0u : mrow[j] != 0;
+    const uint64_t bal = __ballot(sel);
+    if (sel) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
+    cnt += __popcll(bal);
+  }
+  if (lane == 0) *nsel = cnt;
+}
+
 __device__ __forceinline__ int kslot(int c, int r) { return c ^ (r & 15); }
 __device__ __forceinline__ int vslot(int c, int r) { return c ^ ((r & 3) << 2); }
 
@@ -129,7 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t K1[kSub * 256];
   __shared__ __attribute__((aligned(1024))) uint8_t V0[kSub * 256];
   __shared__ __attribute__((aligned(1024))) uint8_t V1[kSub * 256];
-  __shared__ int16_t blist[kMaxBlocks];
+  __shared__ int16_t blist[kListCap];
   __shared__ int nsel_s;
 
   int b, h, i;
@@ -141,21 +160,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int hf = lane >> 5;  // lane half
   const int N = a.seq;
+  const int64_t mrow_index = ((int64_t)b * a.hq + h) * a.nb + i;
+  const int jmax = a.causal ? i : a.nb - 1;
 
-  // ---- compact the mask row: selected key blocks in ascending order
-  if (wave == 0) {
-    const uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * a.nb + i) * a.nb;
-    const int jmax = a.causal ? i : a.nb - 1;
-    int cnt = 0;
-    for (int j0 = 0; j0 <= jmax; j0 += 64) {
-      const int j = j0 + lane;
-      const bool sel = j <= jmax && mrow[j] != 0;
-      const uint64_t bal = __ballot(sel);
-      if (sel) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
-      cnt += __popcll(bal);
-    }
-    if (lane == 0) nsel_s = cnt;
-  }
+  // ---- compact the mask row (its first kListCap blocks; the rest pass by
+  // pass below): selected key blocks in ascending order
+  if (wave == 0) compact_row(a, mrow_index, 0, min(jmax, kListCap - 1), lane, blist, &nsel_s);
 
   // ---- Q rows of this wave as MFMA B operands (registers for the whole loop)
   const int qrow = i * kBlock + wave * 32 + l32;
@@ -171,8 +181,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // Q must have landed before the loop on every path: s_waitcnt vmcnt(0)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  const int nsel = nsel_s;
-  const int nsub = 2 * nsel;
 
   // ---- K/V of this (batch, KV head) as raw buffers; row strides in bytes
   const int kss = (int)(a.k.ss * 2), vss = (int)(a.v.ss * 2);
@@ -337,20 +345,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  if (nsub > 0) {
-    dma_sub(0, K0, V0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
-  __syncthreads();
-  for (int n = 0; n < nsub; n += 2) {
-    if (n + 1 < nsub) dma_sub(n + 1, K1, V1);
-    compute(n, K0, V0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (int cb = 0;;) {
+    const int nsel = nsel_s;
+    const int nsub = 2 * nsel;
+    if (nsub > 0) {
+      dma_sub(0, K0, V0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
     __syncthreads();
-    if (n + 1 >= nsub) break;
-    if (n + 2 < nsub) dma_sub(n + 2, K0, V0);
-    compute(n + 1, K1, V1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    for (int n = 0; n < nsub; n += 2) {
+      if (n + 1 < nsub) dma_sub(n + 1, K1, V1);
+      compute(n, K0, V0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      if (n + 1 >= nsub) break;
+      if (n + 2 < nsub) dma_sub(n + 2, K0, V0);
+      compute(n + 1, K1, V1);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+    }
+    // rows longer than kListCap blocks: the next part of the mask row (every
+    // wave has passed the last barrier, so blist is free)
+    cb += kListCap;
+    if (cb > jmax) break;
+    if (wave == 0) compact_row(a, mrow_index, cb, min(jmax, cb + kListCap - 1), lane, blist, &nsel_s);
     __syncthreads();
   }
 
@@ -379,7 +397,7 @@ constexpr int kF32Tile = 32;      // keys per LDS tile
 __global__ __launch_bounds__(kF32Threads) void attn_fp32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Kt[kF32Tile * kHeadDim];
   __shared__ __attribute__((aligned(16))) float Vs[kF32Tile * kHeadDim];
-  __shared__ int16_t blist[kMaxBlocks];
+  __shared__ int16_t blist[kListCap];
   __shared__ int nsel_s;
 
   int b, h, i;
@@ -392,20 +410,10 @@ __global__ __launch_bounds__(kF32Threads) void attn_fp32_kernel(AttnArgs a) {
   const int N = a.seq;
   const int qrow = i * kBlock + qi;
   const bool qvalid = qrow < N;
+  const int64_t mrow_index = ((int64_t)b * a.hq + h) * a.nb + i;
+  const int jmax = a.causal ? i : a.nb - 1;
 
-  if (tid < 64) {
-    const uint8_t *mrow = a.mask + (((int64_t)b * a.hq + h) * a.nb + i) * a.nb;
-    const int jmax = a.causal ? i : a.nb - 1;
-    int cnt = 0;
-    for (int j0 = 0; j0 <= jmax; j0 += 64) {
-      const int j = j0 + lane;
-      const bool sel = j <= jmax && mrow[j] != 0;
-      const uint64_t bal = __ballot(sel);
-      if (sel) blist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (int16_t)j;
-      cnt += __popcll(bal);
-    }
-    if (lane == 0) nsel_s = cnt;
-  }
+  if (tid < 64) compact_row(a, mrow_index, 0, min(jmax, kListCap - 1), lane, blist, &nsel_s);
 
   float qv[32], ov[32];
   {
@@ -415,12 +423,13 @@ __global__ __launch_bounds__(kF32Threads) void attn_fp32_kernel(AttnArgs a) {
     for (int e = 0; e < 32; ++e) { qv[e] = qvalid ? qp[e] : 0.f; ov[e] = 0.f; }
   }
   __syncthreads();
-  const int nsel = nsel_s;
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
   const float *kb = static_cast<const float *>(a.k.data) + (int64_t)b * a.k.sb + (int64_t)g * a.k.sh;
   const float *vb = static_cast<const float *>(a.v.data) + (int64_t)b * a.v.sb + (int64_t)g * a.v.sh;
 
+  for (int cb = 0;;) {
+  const int nsel = nsel_s;
   for (int n = 0; n < nsel * (kBlock / kF32Tile); ++n) {
     const int j = blist[n / (kBlock / kF32Tile)];
     const int kv0 = j * kBlock + (n % (kBlock / kF32Tile)) * kF32Tile;
@@ -455,6 +464,14 @@ __global__ __launch_bounds__(kF32Threads) void attn_fp32_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+  }
+  // rows longer than kListCap blocks: the next part of the mask row, once
+  // every thread has read this part's count and list
+  cb += kListCap;
+  if (cb > jmax) break;
+  __syncthreads();
+  if (tid < 64) compact_row(a, mrow_index, cb, min(jmax, cb + kListCap - 1), lane, blist, &nsel_s);
+  __syncthreads();
   }
   if (qvalid) {
     const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;

@@ -31,7 +31,9 @@
  *     h / (Hq / Hkv); Hq must be a multiple of Hkv.
  *   - Supported: head_dim 128, block size 128, bf16 throughout or fp32
  *     throughout, any seq >= 1 (a partial last block is handled), any
- *     batch >= 1, up to 2048 blocks per sequence (seq <= 262144).
+ *     batch >= 1, up to 8192 blocks per sequence (seq <= 1048576; scaling
+ *     to a million tokens is the pages' stated future work, Prism review,
+ *     limitations paragraph).
  */
 #ifndef PRISM_H
 #define PRISM_H
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 2
+#define PRISM_ABI_VERSION 3
 
 typedef enum {
   PRISM_OK = 0,
@@ -91,12 +93,24 @@ typedef struct {
   int64_t stride_b, stride_s, stride_h; /* in elements; the head_dim stride is 1 */
 } prism_tensor_t;
 
+/* Storage of a block mask row (query block i of one batch and head).
+ * U8:   nk_blocks bytes, byte j = 1 when key block j is selected, 0 otherwise
+ *       (prism_block_sparse_attn treats any nonzero byte as selected).
+ * BITS: ceil(nk_blocks / 32) 32-bit words, bit (j % 32) of word j / 32 set when
+ *       key block j is selected; bits past nk_blocks are 0 (prism_estimate) or
+ *       ignored (prism_block_sparse_attn). At a million tokens a U8 mask row is
+ *       8 KB and a head's mask 64 MiB; BITS is 8 times smaller. */
+typedef enum { PRISM_MASK_U8 = 0, PRISM_MASK_BITS = 1 } prism_mask_format_t;
+
 typedef struct {
-  uint8_t *data;     /* device, row-major [batch][heads][nq_blocks][nk_blocks]; 1 = compute */
+  void *data;        /* device, row-major [batch][heads][nq_blocks][row], row as `format` says;
+                        4-byte aligned (BITS) or 16-byte aligned (U8) */
   int64_t batch, heads, nq_blocks, nk_blocks;
   int32_t block_size;
   int32_t causal;    /* prism_block_sparse_attn: 1 = blocks above the diagonal are ignored
                         even when set, and key s is masked for query t when s > t */
+  int32_t format;    /* prism_mask_format_t */
+  int32_t reserved;  /* set to 0 */
 } prism_mask_t;
 
 typedef struct {
@@ -160,13 +174,15 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  *   q: post-RoPE queries [batch, seq, Hq, head_dim]; k: post-RoPE keys
  *      [batch, seq, Hkv, head_dim]; same dtype, batch, seq, head_dim.
  *   cfg: band widths, p, causal flag, RoPE layout, temperature mode, workspace.
- *   mask_out: written in full, [batch][Hq][nb][nb] uint8 with
+ *   mask_out: written in full, [batch][Hq][nb][row] in mask_out->format with
  *      nb = ceil(seq / block_size), block_size == cfg->block_size; every byte
  *      of the mask is written (0 above the diagonal when causal).
  * Work: two streaming reads of Q and K (block means and segment energies),
  * a per-head temperature reduction, and per query block the two band score
  * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
- * Four kernels, in order on `stream`.
+ * Four kernels, in order on `stream`. Rows of more than 2048 blocks are
+ * selected by an exact bisection on the same fixed-point masses (one pass
+ * over the row per step), giving the same selection rule.
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream);
@@ -177,7 +193,8 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
  *   A(t) = { s < seq : mask[i][s / B] == 1, and s <= t when mask->causal },
  * keys and values from KV head h / (Hq / Hkv); out[t] = 0 when A(t) is empty.
  *   q, out: [batch, seq, Hq, 128]; k, v: [batch, seq, Hkv, 128]; all one dtype.
- *   mask: [batch][Hq][nb][nb] with block_size 128, e.g. from prism_estimate.
+ *   mask: [batch][Hq][nb][row] with block_size 128 in either format, e.g. from
+ *      prism_estimate.
  * bf16: MFMA products with fp32 accumulation, fp32 online softmax, the
  * probabilities rounded to bf16 for the P.V product; out rounded to bf16.
  * fp32: fp32 throughout. Skipped blocks are neither read nor computed.

@@ -119,3 +119,21 @@ def logit_row(i, nb, causal):
         return i * ((nb + 3) // 4 * 4)
     q, r = i // 4, i % 4
     return 8 * q * (q + 1) + 4 * r * (q + 1)
+
+
+def pack_bits(m: np.ndarray) -> np.ndarray:
+    """uint8 block mask [..., nb] -> the bit-packed form [..., ceil(nb / 32)]
+    int32 (bit j % 32 of word j / 32 set when block j is nonzero)."""
+    nb = m.shape[-1]
+    W = -(-nb // 32)
+    pad = np.zeros(m.shape[:-1] + (W * 32,), np.uint64)
+    pad[..., :nb] = m != 0
+    words = (pad.reshape(m.shape[:-1] + (W, 32)) << np.arange(32, dtype=np.uint64)).sum(-1)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def unpack_bits(w: np.ndarray, nb: int) -> np.ndarray:
+    """Inverse of pack_bits: [..., W] int32 -> uint8 [..., nb]."""
+    u = w.view(np.uint32).astype(np.uint64)
+    bits = (u[..., None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)
+    return bits.reshape(w.shape[:-1] + (w.shape[-1] * 32,))[..., :nb].astype(np.uint8)

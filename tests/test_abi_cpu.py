@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 2
+    assert lib.prism_abi_version() == 3
     for s in range(10):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
@@ -60,7 +60,8 @@ def cfg(**kw):
 
 def mask(seq=4096, heads=32, **kw):
     nb = -(-seq // 128)
-    m = dict(data=FAKE, batch=1, heads=heads, nq_blocks=nb, nk_blocks=nb, block_size=128, causal=1)
+    m = dict(data=FAKE, batch=1, heads=heads, nq_blocks=nb, nk_blocks=nb, block_size=128, causal=1, format=0,
+             reserved=0)
     m.update(kw)
     return PrismMask(**m)
 
@@ -80,7 +81,7 @@ def test_logit_plane_rows_disjoint_and_padded():
     """the documented packed-triangle row starts: row i holds i + 1 floats,
     starts 16-byte aligned, and rows neither overlap nor leave a row short"""
     from tests.parity import logit_row
-    for nb in (1, 2, 5, 8, 1023, 2048):
+    for nb in (1, 2, 5, 8, 1023, 2048, 8192):
         prev_end = 0
         for i in range(nb):
             s = logit_row(i, nb, True)
@@ -154,7 +155,9 @@ E = _abi
     (dict(c=cfg(workspace_bytes=1000)), E.ERR_WORKSPACE),
     (dict(q=tensor(head_dim=64), k=tensor(heads=8, head_dim=64)), E.ERR_UNSUPPORTED),
     (dict(c=cfg(block_size=64)), E.ERR_UNSUPPORTED),
-    (dict(q=tensor(seq=2049 * 128), k=tensor(seq=2049 * 128, heads=8), m=mask(seq=2049 * 128)), E.ERR_UNSUPPORTED),
+    (dict(q=tensor(seq=8193 * 128), k=tensor(seq=8193 * 128, heads=8), m=mask(seq=8193 * 128)), E.ERR_UNSUPPORTED),
+    (dict(m=mask(format=2)), E.ERR_CONFIG),
+    (dict(m=mask(format=1, data=FAKE + 2)), E.ERR_ALIGN),
 ])
 def test_estimate_rejects(lib, case, expect):
     args = dict(q=tensor(), k=tensor(heads=8), c=cfg(), m=mask())
@@ -176,11 +179,40 @@ def test_estimate_rejects(lib, case, expect):
     (dict(m=mask(causal=3)), E.ERR_CONFIG),
     (dict(m=mask(block_size=64)), E.ERR_UNSUPPORTED),
     (dict(v=tensor(heads=8, data=FAKE + 2)), E.ERR_ALIGN),
+    (dict(m=mask(format=7)), E.ERR_CONFIG),
+    (dict(m=mask(format=1, data=FAKE + 1)), E.ERR_ALIGN),
+    (dict(q=tensor(seq=8193 * 128), k=tensor(seq=8193 * 128, heads=8), v=tensor(seq=8193 * 128, heads=8),
+          o=tensor(seq=8193 * 128), m=mask(seq=8193 * 128)), E.ERR_UNSUPPORTED),
 ])
 def test_attention_rejects(lib, case, expect):
     args = dict(q=tensor(), k=tensor(heads=8), v=tensor(heads=8), m=mask(), o=tensor())
     args.update(case)
     assert attn(lib, args["q"], args["k"], args["v"], args["m"], args["o"]) == expect
+
+
+def test_million_token_layout_and_bit_mask_accepted(lib):
+    """8192 blocks (1,048,576 tokens) is the largest supported sequence; a
+    4-byte aligned bit-packed mask passes the same validation as a byte mask
+    (checked through the layout query and the rejection of a NULL workspace,
+    neither of which launches)."""
+    n = 8192 * 128
+    q, k = tensor(seq=n), tensor(seq=n, heads=8)
+    L = PrismWorkspaceLayout()
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg()), ctypes.byref(L)) == 0
+    assert L.nb == 8192 and L.logits_plane >= 8192 * 8193 // 2
+    m = mask(seq=n, format=1, data=FAKE + 4)
+    assert est(lib, q, k, cfg(workspace=0), m) == E.ERR_WORKSPACE  # every other check passed
+
+
+def test_python_mask_descriptor_formats():
+    import torch
+    import block_sparse_attention_band_amd as prism
+    u8 = prism.mask_desc(torch.zeros((1, 2, 40, 40), dtype=torch.uint8), 128, True)
+    assert (u8.format, u8.nq_blocks, u8.nk_blocks) == (_abi.MASK_U8, 40, 40)
+    bits = prism.mask_desc(torch.zeros((1, 2, 40, 2), dtype=torch.int32), 128, True)
+    assert (bits.format, bits.nq_blocks, bits.nk_blocks) == (_abi.MASK_BITS, 40, 40)
+    with pytest.raises(ValueError):
+        prism.mask_desc(torch.zeros((1, 2, 40, 3), dtype=torch.int32), 128, True)
 
 
 def test_layout_descriptors_bhsd_accepted_by_validation(lib):

@@ -16,7 +16,8 @@ torch = pytest.importorskip("torch")
 import block_sparse_attention_band_amd as prism  # noqa: E402
 import oracle.prism_oracle as po  # noqa: E402
 from synth import WORKLOADS, Rope, make_qkv, random_mask, to_f64  # noqa: E402
-from tests.parity import compare_masks, logit_row, oracle_estimate_heads, to_device  # noqa: E402
+from tests.parity import (compare_masks, logit_row, oracle_estimate_heads, pack_bits, to_device,  # noqa: E402
+                          unpack_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -206,6 +207,93 @@ def test_estimator_deterministic_and_overwrites():
         outs.append((m.cpu().numpy(), ws[: L.ksq_offset].cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0])
     assert np.array_equal(outs[0][1], outs[1][1])
+
+
+# ------------------------------------------------- bit-packed masks, long rows
+@pytest.mark.parametrize("name", ["gqa4_ragged", "noncausal", "one_block", "nb_1100", "p_one"])
+def test_estimator_bit_mask_equals_byte_mask(name):
+    """The bit-packed output holds exactly the byte mask's selection, padding
+    bits 0 (same selection code, only the row store differs)."""
+    base, over, cov, layout, rope_layout = SMALL[name]
+    w = WORKLOADS[base].scaled(**over)
+    say(f"[bits] {name}: seq={w.seq} hq={w.hq}")
+    q, k, _ = make_qkv(w, rope_layout=rope_layout, with_v=False)
+    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout})
+    qd, kd = to_device(q, w.dtype, layout), to_device(k, w.dtype, layout)
+    nb = w.nb
+    m8 = prism.estimate(qd, kd, cfg)
+    mb = torch.full((w.batch, w.hq, nb, (nb + 31) // 32), -1, dtype=torch.int32, device="cuda")
+    prism.estimate(qd, kd, cfg, mask_out=mb)
+    torch.cuda.synchronize()
+    g8, gb = m8.cpu().numpy(), mb.cpu().numpy()
+    assert np.array_equal(gb, pack_bits(g8))
+    assert np.array_equal(unpack_bits(gb, nb), g8)
+
+
+@pytest.mark.parametrize("dtype_base,over,density,causal", [
+    ("llama3_8b_32k", dict(seq=2900, hq=4, hkv=1), 0.5, True),
+    ("llama3_8b_32k", dict(seq=1500, hq=2, hkv=1), 0.6, False),
+    ("tiny_fp32_2k", dict(seq=1500, hq=2, hkv=1), 0.5, True),
+])
+def test_attention_bit_mask_equals_byte_mask(dtype_base, over, density, causal):
+    w = WORKLOADS[dtype_base].scaled(**over)
+    say(f"[bits attention] seq={w.seq} {w.dtype} causal={causal}")
+    q, k, v = make_qkv(w)
+    m = random_mask(w.batch, w.hq, w.nb, density, 5, causal)
+    if causal:
+        m[:, :, 2, 5] = 1  # a set bit above the diagonal is ignored in both forms
+    qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
+    outs = []
+    for mk in (torch.from_numpy(m).cuda(), torch.from_numpy(pack_bits(m)).cuda()):
+        o = torch.full_like(qd, float("nan"))
+        prism.block_sparse_attn(qd, kd, vd, mk, causal=causal, out=o)
+        torch.cuda.synchronize()
+        outs.append(o.cpu())
+    assert torch.equal(outs[0].view(torch.int16) if w.dtype == "bf16" else outs[0].view(torch.int32),
+                       outs[1].view(torch.int16) if w.dtype == "bf16" else outs[1].view(torch.int32))
+
+
+LONG = {
+    # rows longer than 2048 blocks take the bisection selection and the
+    # chunked attention block list
+    "nb_4100_causal": (dict(seq=4100 * 128 - 7, hq=1, hkv=1), dict()),
+    "nb_2300_noncausal_p05": (dict(seq=2300 * 128, hq=1, hkv=1, causal=False), dict(p=0.5)),
+    "nb_2100_p_one": (dict(seq=2100 * 128, hq=1, hkv=1), dict(p=1.0)),
+    "nb_8192_max": (dict(seq=8192 * 128, hq=1, hkv=1), dict()),  # 1,048,576 tokens, the largest supported
+}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(LONG))
+def test_long_rows(name):
+    over, cov = LONG[name]
+    w = WORKLOADS["llama3_8b_32k"].scaled(**over)
+    say(f"[long] {name}: seq={w.seq} nb={w.nb} causal={w.causal}")
+    q, k, v = make_qkv(w)
+    cfg = cfg_of(w, **cov)
+    qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
+    m8 = prism.estimate(qd, kd, cfg)
+    mb = prism.estimate(qd, kd, cfg, bits=True)
+    torch.cuda.synchronize()
+    gm = m8.cpu().numpy()
+    assert np.array_equal(mb.cpu().numpy(), pack_bits(gm))
+    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
+                                causal=cfg.causal)
+    st = compare_masks(gm, orc, cfg.p, cfg.causal)
+    say(f"    density={gm.sum() / max(1, st['blocks']):.4f} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
+        f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
+    assert st["unexcused"] == 0, st["where"][:20]
+    # attention over the bit mask on rows past 2048 blocks (several list passes)
+    out = torch.full_like(qd, float("nan"))
+    prism.block_sparse_attn(qd, kd, vd, mb, causal=cfg.causal, out=out)
+    torch.cuda.synchronize()
+    og = out.float().cpu().numpy()
+    assert not np.isnan(og).any()
+    for i in sorted({w.nb - 1, 2047, 2048, w.nb // 2 + 3}):
+        t0, t1 = i * 128, min((i + 1) * 128, w.seq)
+        oo = po.attention_block_row(to_f64(q[0, :, 0, :], w.dtype), to_f64(k[0, :, 0, :], w.dtype),
+                                    to_f64(v[0, :, 0, :], w.dtype), gm[0, 0, i], i, block=128, causal=cfg.causal)
+        check_attention(og[0, t0:t1, 0, :], oo, w.dtype)
 
 
 # ------------------------------------------------------------ attention cases
