@@ -50,9 +50,10 @@ def attention_flops(mask, block, head_dim):
     return 4.0 * block * block * head_dim * below + 2.0 * block * block * head_dim * diag, below + diag
 
 
-def traffic_from_profile():
+def traffic_from_profile(workload):
     """HBM bytes per launch measured by rocprofv3 counters for the current
-    attention kernel source, or None when absent or taken on other source."""
+    attention kernel source on this workload, or None when absent, taken on
+    other source or on another workload."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -61,6 +62,8 @@ def traffic_from_profile():
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("source_sha256") != attn_build_sha() or "hbm_bytes_per_launch" not in vals:
+        return None
+    if vals.get("workload", "llama3_8b_128k") != workload:
         return None
     return float(vals["hbm_bytes_per_launch"])
 
@@ -135,6 +138,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b_128k")
+    ap.add_argument("--mask-bits", action="store_true", help="bit-packed block mask (one bit per block)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baselines")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -174,7 +178,10 @@ def main():
     cfg = prism.EstimatorConfig(block_size=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=True)
     ws = prism.new_workspace(qd, kd, cfg)
     nb = w.nb
-    mask = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.uint8, device="cuda")
+    if args.mask_bits:
+        mask = torch.empty((w.batch, w.hq, nb, (nb + 31) // 32), dtype=torch.int32, device="cuda")
+    else:
+        mask = torch.empty((w.batch, w.hq, nb, nb), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(qd)
 
     def step(ev=None):
@@ -212,12 +219,16 @@ def main():
     log(f"timed: {step_ms:.3f} ms/step (median), estimator {est_ms:.3f} ms, attention {attn_ms:.3f} ms, "
         f"{wall_ms:.3f} ms/step wall incl. cache flush")
 
-    flops, nsel = attention_flops(mask, w.block, w.head_dim)
+    mask_u8 = mask
+    if args.mask_bits:  # unpack (outside the timed region) for the FLOP count and the CPU baseline
+        shifts = torch.arange(32, device="cuda", dtype=torch.int32)
+        mask_u8 = ((mask.unsqueeze(-1) >> shifts) & 1).to(torch.uint8).flatten(-2)[..., :nb].contiguous()
+    flops, nsel = attention_flops(mask_u8, w.block, w.head_dim)
     total_blocks = w.batch * w.hq * nb * (nb + 1) // 2
     density = nsel / total_blocks
     achieved = flops / (attn_ms * 1e-3) / 1e12
     elem = 2 if w.dtype == "bf16" else 4
-    est_bytes = (q.size + k.size) * elem + mask.numel()
+    est_bytes = (q.size + k.size) * elem + mask.numel() * mask.element_size()
     est_gbs = est_bytes / (est_ms * 1e-3) / 1e9
 
     result = {
@@ -226,12 +237,13 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": w.head_dim, "block": w.block, "d_high": w.d_high, "d_low": w.d_low, "p": w.p,
-                   "rope_theta": w.theta, "causal": True, "parallelism": "none"},
+                   "rope_theta": w.theta, "causal": True, "parallelism": "none",
+                   "mask_format": "bits" if args.mask_bits else "u8"},
         "estimator_ms": round(est_ms, 3), "attention_ms": round(attn_ms, 3),
         "wall_ms_per_step_incl_cache_flush": round(wall_ms, 3),
         "mask_density": round(density, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profile(),
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_from_profile(w.name),
                      "kernel": "attn_bf16_kernel", "flops_per_launch": flops},
         "estimator_roofline": {"bound": "hbm", "achieved": round(est_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(est_gbs / PEAK_HBM_GBS, 4), "bytes_per_step": est_bytes},
@@ -274,7 +286,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, mask.cpu().numpy(), w)
+        result["cpu_baseline"] = cpu_baseline(q, k, v, mask_u8.cpu().numpy(), w)
     print(json.dumps(result), flush=True)
 
 

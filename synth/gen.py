@@ -108,6 +108,9 @@ WORKLOADS = {
     "llama3_8b_128k": Workload("llama3_8b_128k", 3, 1, 131072, 32, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
     "qwen3_8b_64k": Workload("qwen3_8b_64k", 4, 1, 65536, 32, 8, 128, "bf16", 1e6, "semantic", True, 0.93),
     "llama3_70b_share_128k": Workload("llama3_70b_share_128k", 5, 1, 131072, 64, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
+    # the length the pages leave to future work: a Llama-3-8B-shaped layer at
+    # 1,048,576 tokens (8192 blocks, the longest supported)
+    "llama3_8b_1m": Workload("llama3_8b_1m", 8, 1, 1 << 20, 32, 8, 128, "bf16", 5e5, "semantic", False, 0.95),
     # RoPE variants the pages say the method carries over to: Qwen3-8B
     # extended from 32K to 128K by YaRN (factor 4), and a Qwen3-VL-8B-shaped
     # layer (interleaved M-RoPE, sections 24/20/20, base 5e6) over a video of

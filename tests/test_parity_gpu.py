@@ -413,14 +413,17 @@ def test_workload_full(name):
     prism.block_sparse_attn(qd, kd, vd, mask, out=out)
     torch.cuda.synchronize()
     gm = mask.cpu().numpy()
-    say(f"    GPU done; oracle estimator over {w.hq} heads")
-    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=True)
+    # beyond 262,144 tokens the oracle checks the first and the last query head
+    heads = list(range(w.hq)) if w.seq <= 262144 else [0, w.hq - 1]
+    say(f"    GPU done; oracle estimator over heads {heads if len(heads) < w.hq else 'all'}")
+    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=w.d_high, d_low=w.d_low, p=w.p, causal=True,
+                                heads=heads)
     st = compare_masks(gm, orc, w.p, True)
     say(f"    density={gm.sum() / st['blocks']:.4f} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
         f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
     assert st["unexcused"] == 0, st["where"][:20]
     # attention: sampled query-block rows under the GPU's mask
-    rows = sample_rows(w, 6 if w.seq > 40000 else 12, seed=w.seed)
+    rows = sample_rows(w, 3 if w.seq > 262144 else (6 if w.seq > 40000 else 12), seed=w.seed)
     say(f"    oracle attention on rows {rows}")
     og = out.float().cpu().numpy()
     assert not np.isnan(og).any()
