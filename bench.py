@@ -77,6 +77,39 @@ def attn_build_sha():
     return h.hexdigest()
 
 
+def machine_microbench():
+    """Context for the roofline fractions, measured on this GPU: a plain
+    device-to-device copy of 1 GiB (GB/s of bytes read + written) and a large
+    bf16 GEMM through torch.matmul (the vendor BLAS), best of 5 each."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return min(ts)
+
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    copy_ms = best(lambda: dst.copy_(src))
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    gemm_ms = best(lambda: torch.matmul(a, b, out=c))
+    del a, b, c
+    return {"copy_gbs": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+            "gemm_bf16_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
+
+
 def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
     """The CPU oracle on a bounded sample of the same layer, extrapolated to
     ms per layer: the estimator head by head (KV group by KV group) and the
@@ -140,6 +173,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b_128k")
     ap.add_argument("--mask-bits", action="store_true", help="bit-packed block mask (one bit per block)")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baselines")
+    ap.add_argument("--no-machine", action="store_true", help="skip the copy / GEMM microbenchmarks")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB), the "
@@ -283,6 +317,10 @@ def main():
         result["dense_ms"] = dense
         result["speedup_vs_dense"] = round(best / step_ms, 3)
         log(f"dense: {dense}")
+
+    if not args.no_machine:
+        result["machine"] = machine_microbench()
+        log(f"machine: {result['machine']}")
 
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
