@@ -27,7 +27,11 @@
 //   holding more than 64 entries is refined on the next key bits; rows that
 //   stay unresolved fall back to a bisection over the fp32 bit pattern of
 //   the threshold. The first branch's selection stays in registers; the
-//   union of both is written as the mask row, zeros included.
+//   union of both is written as the mask row (bytes or bits), zeros
+//   included.
+// topp_long_kernel: rows of more than 2048 blocks (up to 8192), which do not
+//   fit in registers: the same rule by bisection on the key over the same
+//   fixed-point masses, the row re-read from the logit plane at every pass.
 #include "prism_kernels.h"
 
 namespace prism {
@@ -478,8 +482,13 @@ constexpr int kScoreTilesPerWg = 4;  // key tiles one workgroup sweeps along its
 // 8c + 4hf + e for MFMA e (A and B agree, so each dim enters once).
 // LO8, HI8 >= 0: both segment boundaries are multiples of 8 (lo = 8 LO8,
 // hi = 8 HI8), every chunk lies in one segment known at compile time.
-// Otherwise each chunk feeds all three accumulators with the dims of the
-// other segments zeroed (three times the MFMAs, for unusual band widths).
+// LO8 == kRuntime8: both boundaries are multiples of 8 given at run time;
+// the segment of each chunk is a wave-uniform branch.
+// Otherwise (LO8 < 0) each chunk feeds all three accumulators with the dims
+// of the other segments zeroed (three times the MFMAs, for band widths that
+// are not multiples of 8).
+constexpr int kRuntime8 = 100;
+
 template <int LO8, int HI8>
 __device__ __forceinline__ void score_tile(const float4 (&qa)[16], const float4 *kr, int krow, int hf, int lo, int hi,
                                            int overlap, f32x16 &acc0, f32x16 &acc1, f32x16 &acc2) {
@@ -489,10 +498,12 @@ __device__ __forceinline__ void score_tile(const float4 (&qa)[16], const float4 
     const float qv[4] = {qa[c].x, qa[c].y, qa[c].z, qa[c].w};
     const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
     if constexpr (LO8 >= 0) {
-      if (c < LO8) {
+      const int lo8 = LO8 == kRuntime8 ? lo >> 3 : LO8;
+      const int hi8 = LO8 == kRuntime8 ? hi >> 3 : HI8;
+      if (c < lo8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[e], kv[e], acc0, 0, 0, 0);
-      } else if (c < HI8) {
+      } else if (c < hi8) {
         if (overlap) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(qv[e], kv[e], acc1, 0, 0, 0);
@@ -771,7 +782,8 @@ constexpr int kLongChunks = kMaxBlocks / 2048;
 
 __device__ void select_row_long(const float *row, int nc, float p, int lane, uint32_t (&sel)[kLongChunks]) {
   const int nch = (nc + 2047) / 2048;
-  auto key_of = [&](int c, int e4, float (&x)[4]) {
+  // logits of elements 4 e4 .. 4 e4 + 3 of chunk c (-inf past the row)
+  auto logits4 = [&](int c, int e4, float (&x)[4]) {
     const int j = 2048 * c + 4 * lane + 256 * e4;
     float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
@@ -781,47 +793,56 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
     x[3] = (j + 3 < nc) ? t.w : -INFINITY;
   };
   float mx = -INFINITY;
-  _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c) {
+    if (c >= nch) break;
 #pragma unroll
     for (int e4 = 0; e4 < 8; ++e4) {
       float x[4];
-      key_of(c, e4, x);
+      logits4(c, e4, x);
       mx = fmaxf(fmaxf(mx, fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
     }
+  }
   mx = wave_max(mx);
-  // S(t): fixed-point mass of the entries with key >= t (t = 1: all of them;
-  // exp2(-inf) = 0 marks the inadmissible ones)
+  // S(t): fixed-point mass of the entries with key >= t (or > t); exp2(-inf)
+  // = 0 marks the inadmissible entries, so S(1) is the whole row's mass
   auto mass_from = [&](uint32_t t, bool strict) -> unsigned long long {
     unsigned long long sl = 0;
-    _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+    for (int c = 0; c < kLongChunks; ++c) {
+      if (c >= nch) break;
 #pragma unroll
       for (int e4 = 0; e4 < 8; ++e4) {
         float x[4];
-        key_of(c, e4, x);
+        logits4(c, e4, x);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
           if (strict ? k > t : k >= t) sl += fixed_mass(k);
         }
       }
+    }
     return lane63(scan_add(sl));
   };
 #pragma unroll
   for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
   if (p >= 1.0f) {
-    _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+    for (int c = 0; c < kLongChunks; ++c) {
+      if (c >= nch) break;
 #pragma unroll
       for (int e4 = 0; e4 < 8; ++e4) {
         float x[4];
-        key_of(c, e4, x);
+        logits4(c, e4, x);
 #pragma unroll
         for (int m = 0; m < 4; ++m) sel[c] |= (x[m] != -INFINITY ? 1u : 0u) << (4 * e4 + m);
       }
+    }
     return;
   }
   const unsigned long long Z = mass_from(1u, false);
   const unsigned long long target = (unsigned long long)ceil((double)Z * (double)p);
-  // invariant: S(lo) >= target > S(hi); every key is <= 1.0f's
+  // invariant: S(lo) >= target > S(hi); every key is at most 1.0f's
   uint32_t lo = 1u, hi = 0x3F800001u;
   while (hi - lo > 1u) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
@@ -832,12 +853,15 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
   const unsigned long long mT = fixed_mass(T);  // > 0: S(T) > S(T + 1)
   const unsigned long long take = (target - above + mT - 1) / mT;
   // keep key > T, and the first `take` entries with key T in block order
+  // (chunk, then e4, then lane, then element)
   unsigned long long rank0 = 0;
-  _Pragma("unroll") for (int c = 0; c < kLongChunks; ++c) if (c < nch)
+#pragma unroll
+  for (int c = 0; c < kLongChunks; ++c) {
+    if (c >= nch) break;
 #pragma unroll
     for (int e4 = 0; e4 < 8; ++e4) {
       float x[4];
-      key_of(c, e4, x);
+      logits4(c, e4, x);
       uint32_t tie = 0;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -855,6 +879,7 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
         }
       rank0 += (unsigned long long)wave_sum_i(cnt);
     }
+  }
 }
 
 // Rows of more than kShortRow blocks: one workgroup = two rows x two
@@ -895,13 +920,17 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
   const dim3 grid(per_head * a.nh * a.batch);  // heads x (full chunks, then remainders)
   const bool def = a.seg_lo == 32 && a.seg_hi == 64, equal = a.seg_lo == 0 && a.seg_hi == 128;
+  const bool by8 = a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0;
   if (a.pervec) {
     if (def) hipLaunchKernelGGL((score_kernel<4, 8, true>), grid, dim3(256), 0, s, a);
+    else if (by8) hipLaunchKernelGGL((score_kernel<kRuntime8, 0, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((score_kernel<-1, -1, true>), grid, dim3(256), 0, s, a);
   } else if (def) {
     hipLaunchKernelGGL((score_kernel<4, 8, false>), grid, dim3(256), 0, s, a);
   } else if (equal) {
     hipLaunchKernelGGL((score_kernel<0, 16, false>), grid, dim3(256), 0, s, a);
+  } else if (by8) {
+    hipLaunchKernelGGL((score_kernel<kRuntime8, 0, false>), grid, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((score_kernel<-1, -1, false>), grid, dim3(256), 0, s, a);
   }
