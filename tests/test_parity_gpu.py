@@ -416,6 +416,74 @@ def test_attention_on_estimator_mask_and_deterministic():
     check_attention(og, oo, "bf16")
 
 
+# ------------------------------------------------- graph capture, two streams
+def test_graph_capture_replays_match_eager():
+    """The library allocates nothing and never synchronises, so both calls can
+    be captured into one HIP graph; every replay (with eager work and
+    synchronisation in between) must give the eager bytes."""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=5000, hq=8, hkv=2)
+    q, k, v = make_qkv(w)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    cfg = cfg_of(w)
+    ws = prism.new_workspace(qd, kd, cfg)
+    mask = torch.empty((1, w.hq, w.nb, w.nb), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qd)
+    prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+    prism.block_sparse_attn(qd, kd, vd, mask, out=out)
+    torch.cuda.synchronize()
+    ref_m, ref_o = mask.clone(), out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+            prism.block_sparse_attn(qd, kd, vd, mask, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(3):
+        mask.fill_(9)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(mask, ref_m), r
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)), r
+        _ = (qd.float().sum() + 1).item()  # eager work between replays
+
+
+def test_two_streams_concurrent_calls():
+    """Calls are reentrant: two problems on two streams (own workspaces and
+    outputs) give the same bytes as run alone."""
+    ws_ = [WORKLOADS["llama3_8b_32k"].scaled(seq=4000, hq=4, hkv=1),
+           WORKLOADS["qwen3_8b_64k"].scaled(seq=3000, hq=8, hkv=2)]
+    data = []
+    for w in ws_:
+        q, k, v = make_qkv(w)
+        qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+        cfg = cfg_of(w)
+        m = prism.estimate(qd, kd, cfg)
+        o = prism.block_sparse_attn(qd, kd, vd, m)
+        torch.cuda.synchronize()
+        data.append((qd, kd, vd, cfg, m.clone(), o.clone(), prism.new_workspace(qd, kd, cfg)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (qd, kd, vd, cfg, _, _, ws), st in zip(data, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            m = torch.empty((1, qd.shape[2], (qd.shape[1] + 127) // 128, (qd.shape[1] + 127) // 128),
+                            dtype=torch.uint8, device="cuda")
+            o = torch.empty_like(qd)
+            for _ in range(3):
+                prism.estimate(qd, kd, cfg, workspace=ws, mask_out=m)
+                prism.block_sparse_attn(qd, kd, vd, m, out=o)
+            outs.append((m, o))
+    torch.cuda.synchronize()
+    for (m, o), d in zip(outs, data):
+        assert torch.equal(m, d[4])
+        assert torch.equal(o.view(torch.int16), d[5].view(torch.int16))
+
+
 # ------------------------------------------------------------ full workloads
 def sample_rows(w, n_rows, seed):
     rng = np.random.default_rng([seed, 7])
