@@ -31,7 +31,9 @@ METRIC = "estimator ms + block-sparse prefill ms/layer at 128K; speedup vs dense
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_band_amd", "csrc", "sparse_attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_bf16_llama3_8b_128k_traffic.txt")
+def traffic_file(workload):
+    """rocprofv3 traffic summary of the attention kernel on this workload"""
+    return os.path.join(ROOT, "profiles", f"sparse_attn_bf16_{workload}_traffic.txt")
 
 
 def log(msg):
@@ -54,16 +56,15 @@ def traffic_from_profile(workload):
     """HBM bytes per launch measured by rocprofv3 counters for the current
     attention kernel source on this workload, or None when absent, taken on
     other source or on another workload."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(workload)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     if vals.get("source_sha256") != attn_build_sha() or "hbm_bytes_per_launch" not in vals:
-        return None
-    if vals.get("workload", "llama3_8b_128k") != workload:
         return None
     return float(vals["hbm_bytes_per_launch"])
 
