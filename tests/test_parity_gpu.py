@@ -256,18 +256,19 @@ def test_attention_bit_mask_equals_byte_mask(dtype_base, over, density, causal):
 LONG = {
     # rows longer than 2048 blocks take the bisection selection and the
     # chunked attention block list
-    "nb_4100_causal": (dict(seq=4100 * 128 - 7, hq=1, hkv=1), dict()),
-    "nb_2300_noncausal_p05": (dict(seq=2300 * 128, hq=1, hkv=1, causal=False), dict(p=0.5)),
-    "nb_2100_p_one": (dict(seq=2100 * 128, hq=1, hkv=1), dict(p=1.0)),
-    "nb_8192_max": (dict(seq=8192 * 128, hq=1, hkv=1), dict()),  # 1,048,576 tokens, the largest supported
+    "nb_4100_causal": ("llama3_8b_32k", dict(seq=4100 * 128 - 7, hq=1, hkv=1), dict()),
+    "nb_2300_noncausal_p05": ("llama3_8b_32k", dict(seq=2300 * 128, hq=1, hkv=1, causal=False), dict(p=0.5)),
+    "nb_2100_p_one": ("llama3_8b_32k", dict(seq=2100 * 128, hq=1, hkv=1), dict(p=1.0)),
+    "nb_8192_max": ("llama3_8b_32k", dict(seq=8192 * 128, hq=1, hkv=1), dict()),  # 1,048,576 tokens, the largest
+    "nb_2100_fp32": ("tiny_fp32_2k", dict(seq=2100 * 128 - 3, hq=1, hkv=1), dict()),
 }
 
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(LONG))
 def test_long_rows(name):
-    over, cov = LONG[name]
-    w = WORKLOADS["llama3_8b_32k"].scaled(**over)
+    base, over, cov = LONG[name]
+    w = WORKLOADS[base].scaled(**over)
     say(f"[long] {name}: seq={w.seq} nb={w.nb} causal={w.causal}")
     q, k, v = make_qkv(w)
     cfg = cfg_of(w, **cov)
