@@ -123,6 +123,14 @@ def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     G = w.hq // w.hkv
     t0 = time.perf_counter()
     heads_done = 0
@@ -156,7 +164,7 @@ def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
     total_blocks = int(np.tril(mask_np[0]).sum())
     attn_ms = t_attn / max(1, blocks_done) * total_blocks * 1e3
     return {
-        "value": round(est_ms + attn_ms, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+        "value": round(est_ms + attn_ms, 1), "unit": "ms", "cores": int(threads), "cpu_model": cpu_model, "kind": "oracle",
         "sample": (f"float64 numpy oracle; estimator on {heads_done} of {w.hq} query heads ({t_est:.1f} s), "
                    f"attention on query-block rows {rows} of heads 0..{used[-1][0]} ({len(used)} rows, "
                    f"{blocks_done} selected blocks, {t_attn:.1f} s); both extrapolated linearly to the whole "

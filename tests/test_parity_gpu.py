@@ -298,32 +298,34 @@ def test_long_rows(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("bits", [False, True])
-def test_attention_head_pairs_long(bits):
+@pytest.mark.parametrize("bits,batch,causal", [(False, 1, True), (True, 1, True), (False, 2, False)])
+def test_attention_head_pairs_long(bits, batch, causal):
     """Past 3072 blocks, two query heads of a KV group share one workgroup and
     its K/V tiles: heads with different masks, one head with empty rows while
     its pair partner computes, a ragged end, rows on both sides of the
-    2048-block list passes."""
-    w = WORKLOADS["llama3_8b_32k"].scaled(seq=3100 * 128 - 50, hq=4, hkv=2)
-    say(f"[pairs] seq={w.seq} nb={w.nb} hq={w.hq} hkv={w.hkv} bits={bits}")
+    2048-block list passes; batch 2 and the non-causal form too."""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=3100 * 128 - 50, hq=4, hkv=2, batch=batch)
+    say(f"[pairs] seq={w.seq} nb={w.nb} hq={w.hq} hkv={w.hkv} batch={batch} causal={causal} bits={bits}")
     q, k, v = make_qkv(w)
-    m = random_mask(1, w.hq, w.nb, 0.6, 17, True)
-    m[0, 1, 1500] = 0   # head 1 computes nothing on this row; head 0 (its pair) does
-    m[0, 2, :, 2048:] = 0  # head 2 selects nothing past the first list pass
+    m = random_mask(batch, w.hq, w.nb, 0.6, 17, causal)
+    m[:, 1, 1500] = 0   # head 1 computes nothing on this row; head 0 (its pair) does
+    m[:, 2, :, 2048:] = 0  # head 2 selects nothing past the first list pass
     qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
     md = torch.from_numpy(pack_bits(m) if bits else m).cuda()
     out = torch.full_like(qd, float("nan"))
-    prism.block_sparse_attn(qd, kd, vd, md, out=out)
+    prism.block_sparse_attn(qd, kd, vd, md, causal=causal, out=out)
     torch.cuda.synchronize()
     og = out.float().cpu().numpy()
     assert not np.isnan(og).any()
-    assert np.all(og[0, 1500 * 128: 1501 * 128, 1] == 0)
-    for h in range(w.hq):
-        for i in (0, 1500, 2047, 2048, w.nb - 1):
-            t0, t1 = i * 128, min((i + 1) * 128, w.seq)
-            oo = po.attention_block_row(to_f64(q[0, :, h, :], "bf16"), to_f64(k[0, :, h // 2, :], "bf16"),
-                                        to_f64(v[0, :, h // 2, :], "bf16"), m[0, h, i], i, block=128, causal=True)
-            check_attention(og[0, t0:t1, h, :], oo, "bf16")
+    assert np.all(og[:, 1500 * 128: 1501 * 128, 1] == 0)
+    for bb in range(batch):
+        for h in range(w.hq):
+            for i in (0, 1500, 2047, 2048, w.nb - 1):
+                t0, t1 = i * 128, min((i + 1) * 128, w.seq)
+                oo = po.attention_block_row(to_f64(q[bb, :, h, :], "bf16"), to_f64(k[bb, :, h // 2, :], "bf16"),
+                                            to_f64(v[bb, :, h // 2, :], "bf16"), m[bb, h, i], i, block=128,
+                                            causal=causal)
+                check_attention(og[bb, t0:t1, h, :], oo, "bf16")
 
 
 # ------------------------------------------------------------ attention cases
