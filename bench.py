@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -70,9 +71,14 @@ def traffic_from_profile(workload):
 
 
 def attn_build_sha():
-    """sha256 over the attention kernel source and the hipcc flags it is built with"""
+    """sha256 over the attention kernel's code (comments and whitespace
+    stripped, so a comment edit keeps a measurement valid) and the hipcc
+    flags it is built with"""
     from block_sparse_attention_band_amd import build
-    h = hashlib.sha256(open(ATTN_SRC, "rb").read())
+    src = open(ATTN_SRC).read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    h = hashlib.sha256(" ".join(src.split()).encode())
     flags = [f for f in build.flags() if not f.startswith("/")] + build.EXTRA.get("sparse_attn.hip", [])
     h.update(" ".join(flags).encode())
     return h.hexdigest()

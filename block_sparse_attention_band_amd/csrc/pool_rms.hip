@@ -14,7 +14,10 @@
 // tau_kernel: per query head, fixed-order fp64 sums of those segment
 //   energies over all blocks give R = sqrt(energy / (nb * |D|)) for the
 //   high band, the low band and the full spectrum of Qbar and Kbar, and
-//   tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full)).
+//   tau_z = R(Qbar,D_z) R(Kbar,D_z) / (R(Qbar,D_full) R(Kbar,D_full)) (the
+//   adopted reading), or R(Qbar,D_z) R(Kbar,D_z) (unit-energy reading), or 1
+//   (no temperature, and the per-vector reading, which scales per pooled
+//   vector in the score kernel instead).
 #include "prism_kernels.h"
 
 namespace prism {

@@ -11,14 +11,20 @@
 //     list of key blocks in LDS, 2048 blocks of the row at a time; only those
 //     blocks are loaded and computed.
 //   * Keys and values stream in sub-tiles of 64 tokens through two LDS
-//     buffers: the next sub-tile's global loads are in flight while the
-//     current one is computed. V is transposed on its way into LDS.
+//     buffers by direct global-to-LDS loads (buffer_load ... lds, no staging
+//     registers): the next sub-tile's loads are in flight while the current
+//     one is computed. Rows sit in LDS with XOR-swizzled 16-byte chunks so
+//     every operand read is free of bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers. Key
 //     rows are fed to the MFMA in a permuted order chosen so that each lane's
 //     16 accumulator registers per 32-key tile hold, for k-step v, eight
 //     consecutive keys 16v + 8*(lane/32) + 0..7 of one query column. The
 //     softmax'd values are therefore already the B operand (P^T) of
-//     O^T += V^T P^T, and V^T is read with one 16-byte LDS load per MFMA.
+//     O^T += V^T P^T. V^T operands come from V's row-major LDS tile through
+//     gfx950's transposing LDS read (two ds_read_b64_tr_b16 per operand).
+//     All K fragments of a sub-tile are read before its first MFMA and all
+//     V^T fragments right after its last S MFMA, and the wave raises its
+//     issue priority over the P.V MFMAs.
 //   * Online softmax in fp32 registers (base 2, scale folded into one FMA).
 //     The exponent reference only moves, and O and the row sum are only
 //     rescaled, when some query's running max has grown by more than 8 in
