@@ -57,6 +57,15 @@ int check_qk(const prism_tensor_t *q, const prism_tensor_t *k) {
   return PRISM_OK;
 }
 
+// Launch geometry: the largest grid (one 512-thread workgroup per batch,
+// query head and query block) stays below 2^32 work-items, and the batch,
+// a second grid dimension of the estimator, below 65536.
+int check_launch(int64_t batch, int64_t heads, int64_t nb) {
+  if (batch > 65535) return PRISM_ERR_UNSUPPORTED;
+  if (batch * heads * nb * 512 > (int64_t)0xFFFFFFFF) return PRISM_ERR_UNSUPPORTED;
+  return PRISM_OK;
+}
+
 int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (!cfg) return PRISM_ERR_NULL;
   if (cfg->block_size < 1) return PRISM_ERR_CONFIG;
@@ -69,6 +78,14 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (cfg->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
   if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
+}
+
+int check_estimate_args(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg) {
+  int st = check_qk(q, k);
+  if (st) return st;
+  st = check_cfg(cfg, q->seq);
+  if (st) return st;
+  return check_launch(q->batch, q->heads, (q->seq + cfg->block_size - 1) / cfg->block_size);
 }
 
 void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
@@ -133,9 +150,7 @@ const char *prism_status_str(int status) {
 
 int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                                     prism_workspace_layout_t *layout) {
-  int st = check_qk(q, k);
-  if (st) return st;
-  st = check_cfg(cfg, q->seq);
+  const int st = check_estimate_args(q, k, cfg);
   if (st) return st;
   if (!layout) return PRISM_ERR_NULL;
   make_layout(q, k, cfg, layout);
@@ -150,9 +165,7 @@ size_t prism_estimate_workspace_bytes(const prism_tensor_t *q, const prism_tenso
 
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream) {
-  int st = check_qk(q, k);
-  if (st) return st;
-  st = check_cfg(cfg, q->seq);
+  int st = check_estimate_args(q, k, cfg);
   if (st) return st;
   prism_workspace_layout_t L;
   make_layout(q, k, cfg, &L);
@@ -265,6 +278,7 @@ int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, co
   if (mask->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
   const int64_t nb = (q->seq + kBlock - 1) / kBlock;
   if (nb > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
+  if ((st = check_launch(q->batch, q->heads, nb))) return st;
   if (mask->batch != q->batch || mask->heads != q->heads || mask->nq_blocks != nb || mask->nk_blocks != nb)
     return PRISM_ERR_SHAPE;
   if ((st = check_mask_format(mask))) return st;

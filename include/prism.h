@@ -33,7 +33,9 @@
  *     throughout, any seq >= 1 (a partial last block is handled), any
  *     batch >= 1, up to 8192 blocks per sequence (seq <= 1048576; scaling
  *     to a million tokens is the pages' stated future work, Prism review,
- *     limitations paragraph).
+ *     limitations paragraph). Launch limits: batch <= 65535 and
+ *     batch * query heads * blocks * 512 < 2^32; larger problems return
+ *     PRISM_ERR_UNSUPPORTED (split them by batch or head).
  */
 #ifndef PRISM_H
 #define PRISM_H

@@ -157,6 +157,11 @@ E = _abi
     (dict(c=cfg(block_size=64)), E.ERR_UNSUPPORTED),
     (dict(q=tensor(seq=8193 * 128), k=tensor(seq=8193 * 128, heads=8), m=mask(seq=8193 * 128)), E.ERR_UNSUPPORTED),
     (dict(m=mask(format=2)), E.ERR_CONFIG),
+    # launch limits: a second grid dimension of 65536, 2^32 work-items
+    (dict(q=tensor(batch=65536, heads=1, seq=128), k=tensor(batch=65536, heads=1, seq=128),
+          m=mask(seq=128, heads=1, batch=65536)), E.ERR_UNSUPPORTED),
+    (dict(q=tensor(heads=4096, seq=8192 * 128), k=tensor(heads=8, seq=8192 * 128),
+          m=mask(seq=8192 * 128, heads=4096)), E.ERR_UNSUPPORTED),
     (dict(m=mask(format=1, data=FAKE + 2)), E.ERR_ALIGN),
 ])
 def test_estimate_rejects(lib, case, expect):
@@ -180,6 +185,8 @@ def test_estimate_rejects(lib, case, expect):
     (dict(m=mask(block_size=64)), E.ERR_UNSUPPORTED),
     (dict(v=tensor(heads=8, data=FAKE + 2)), E.ERR_ALIGN),
     (dict(m=mask(format=7)), E.ERR_CONFIG),
+    (dict(q=tensor(heads=4096, seq=8192 * 128), k=tensor(heads=8, seq=8192 * 128), v=tensor(heads=8, seq=8192 * 128),
+          o=tensor(heads=4096, seq=8192 * 128), m=mask(seq=8192 * 128, heads=4096)), E.ERR_UNSUPPORTED),
     (dict(m=mask(format=1, data=FAKE + 1)), E.ERR_ALIGN),
     (dict(q=tensor(seq=8193 * 128), k=tensor(seq=8193 * 128, heads=8), v=tensor(seq=8193 * 128, heads=8),
           o=tensor(seq=8193 * 128), m=mask(seq=8193 * 128)), E.ERR_UNSUPPORTED),
