@@ -192,6 +192,43 @@ def test_estimator_peaked_rows_deep_tail(a, p):
                           prism.EstimatorConfig(p=p))
 
 
+def test_estimator_zero_keys_degenerate_temperature():
+    """K = 0: every band RMS of K is 0, so the temperature falls back to 1
+    (counted as degenerate) and every score of a row is 0 -- uniform rows."""
+    from synth import f32_to_bf16_bits
+    rng = np.random.default_rng(5)
+    N = 40 * 128 - 9
+    q = f32_to_bf16_bits(rng.standard_normal((1, N, 2, 128)).astype(np.float32))
+    k = f32_to_bf16_bits(np.zeros((1, N, 1, 128), np.float32))
+    gm, orc = _estimate_and_compare("zero keys", q, k, "bf16", prism.EstimatorConfig(p=0.9))
+    assert all(r["degenerate"] == 2 for r in orc.values())
+    for i in (0, 7, 39):
+        assert gm[0, 0, i, : i + 1].sum() == int(np.ceil(0.9 * (i + 1) - 1e-12))
+
+
+@pytest.mark.parametrize("scale", [16.0, 64.0])
+def test_attention_large_logits(scale):
+    """Queries scaled up so the softmax rows are nearly one-hot and running
+    maxima jump by far more than the lazy-rescale slack, sub-tile after
+    sub-tile (bf16 and fp32 paths)."""
+    for base, seq in (("llama3_8b_32k", 2600), ("tiny_fp32_2k", 900)):
+        w = WORKLOADS[base].scaled(seq=seq, hq=2, hkv=1)
+        q, k, v = make_qkv(w)
+        q64 = to_f64(q, w.dtype) * scale
+        if w.dtype == "bf16":
+            from synth import f32_to_bf16_bits
+            q = f32_to_bf16_bits(q64.astype(np.float32))
+        else:
+            q = q64.astype(np.float32)
+        mask = random_mask(1, w.hq, w.nb, 0.7, 23, True)
+        qd, kd, vd = (to_device(x, w.dtype) for x in (q, k, v))
+        out = torch.full_like(qd, float("nan"))
+        prism.block_sparse_attn(qd, kd, vd, torch.from_numpy(mask).cuda(), out=out)
+        torch.cuda.synchronize()
+        say(f"[large logits] {base} x{scale}")
+        check_attention(out.float().cpu().numpy(), oracle_attention(q, k, v, mask, w.dtype, True), w.dtype)
+
+
 def test_estimator_deterministic_and_overwrites():
     w = WORKLOADS["llama3_8b_32k"].scaled(seq=5000, hq=8, hkv=2)
     q, k, _ = make_qkv(w, with_v=False)
