@@ -30,8 +30,9 @@
 //   union of both is written as the mask row (bytes or bits), zeros
 //   included.
 // topp_long_kernel: rows of more than 2048 blocks (up to 8192), which do not
-//   fit in registers: the same rule by bisection on the key over the same
-//   fixed-point masses, the row re-read from the logit plane at every pass.
+//   fit in registers: the same rule by a five-pass radix select on the key
+//   over the same fixed-point masses, the row re-read from the logit plane at
+//   every pass.
 #include "prism_kernels.h"
 
 namespace prism {
@@ -772,15 +773,22 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
 // is block 2048 c + 4 l + 256 (k / 4) + k % 4). The selection rule is
 // select_row_hist's: masses m = floor(e 2^31) of e = exp2(L - max), target
 // ceil(p Z), the shortest prefix of (e descending, block ascending) whose
-// mass reaches the target. It is found by bisection on the key (the bit
-// pattern of e, monotone in e): T = the largest key with
-// mass(key >= T) >= target; every key above T is kept, and of the entries
-// with key T the first ceil((target - mass(key > T)) / m(T)) in block order.
-// Keys are recomputed from the logits at every pass (about 32 passes over
-// the row, read from L2). sel[c] receives this lane's bits of chunk c.
+// mass reaches the target. It is found by a radix select on the key (the
+// bit pattern of e, monotone in e): five passes over the row, the first
+// binning the keys by octave (exponent 64..127, all smaller e in the lowest
+// bin: their masses are 0), the others by the next 6, 6, 6 and 5 mantissa
+// bits of the keys that share the prefix found so far (fixed-point masses,
+// exact in any order), each keeping the bin where the mass from the top
+// reaches the target. That gives the key T with
+// mass(key >= T) >= target > mass(key > T); every key above T is kept, and
+// of the entries with key T the first ceil((target - mass(key > T)) / m(T))
+// in block order. Keys are recomputed from the logits at every pass (the
+// row stays in L2). sel[c] receives this lane's bits of chunk c; bins is
+// the wave's 64-entry LDS histogram.
 constexpr int kLongChunks = kMaxBlocks / 2048;
 
-__device__ void select_row_long(const float *row, int nc, float p, int lane, uint32_t (&sel)[kLongChunks]) {
+__device__ void select_row_long(const float *row, int nc, float p, int lane, unsigned long long *bins,
+                                uint32_t (&sel)[kLongChunks]) {
   const int nch = (nc + 2047) / 2048;
   // logits of elements 4 e4 .. 4 e4 + 3 of chunk c (-inf past the row)
   auto logits4 = [&](int c, int e4, float (&x)[4]) {
@@ -804,26 +812,6 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
     }
   }
   mx = wave_max(mx);
-  // S(t): fixed-point mass of the entries with key >= t (or > t); exp2(-inf)
-  // = 0 marks the inadmissible entries, so S(1) is the whole row's mass
-  auto mass_from = [&](uint32_t t, bool strict) -> unsigned long long {
-    unsigned long long sl = 0;
-#pragma unroll
-    for (int c = 0; c < kLongChunks; ++c) {
-      if (c >= nch) break;
-#pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4) {
-        float x[4];
-        logits4(c, e4, x);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
-          if (strict ? k > t : k >= t) sl += fixed_mass(k);
-        }
-      }
-    }
-    return lane63(scan_add(sl));
-  };
 #pragma unroll
   for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
   if (p >= 1.0f) {
@@ -840,17 +828,48 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
     }
     return;
   }
-  const unsigned long long Z = mass_from(1u, false);
-  const unsigned long long target = (unsigned long long)ceil((double)Z * (double)p);
-  // invariant: S(lo) >= target > S(hi); every key is at most 1.0f's
-  uint32_t lo = 1u, hi = 0x3F800001u;
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    if (mass_from(mid, false) >= target) lo = mid; else hi = mid;
+  // radix levels: the exponent (octaves), then mantissa bits 22..17, 16..11,
+  // 10..5 and 4..0; exp2(-inf) = 0 marks the inadmissible entries (never
+  // counted)
+  unsigned long long target = 0, above = 0;  // above: mass of the keys above the prefix's range
+  uint32_t prefix = 0;
+#pragma unroll 1
+  for (int level = 0; level < 5; ++level) {
+    const int shift = level == 0 ? 23 : 23 - 6 * level + (level == 4 ? 1 : 0);  // 23, 17, 11, 5, 0
+    const int width = level == 0 ? 0 : (level == 4 ? 5 : 6);                    // prefix bits kept per level
+    bins[lane] = 0ull;
+    wave_lds_sync();
+#pragma unroll
+    for (int c = 0; c < kLongChunks; ++c) {
+      if (c >= nch) break;
+#pragma unroll
+      for (int e4 = 0; e4 < 8; ++e4) {
+        float x[4];
+        logits4(c, e4, x);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
+          if (k != 0u && (level == 0 || (k >> (shift + width)) == prefix)) {
+            const uint32_t bin = level == 0 ? (uint32_t)max((int)(k >> 23) - 64, 0)
+                                            : (k >> shift) & ((1u << width) - 1u);
+            atomicAdd(&bins[bin], (unsigned long long)fixed_mass(k));
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+    const unsigned long long mass = bins[63 - lane];  // lane 0 holds the largest keys
+    const unsigned long long cum = scan_add(mass);     // mass of this bin and every bin above it
+    if (level == 0) target = (unsigned long long)ceil((double)lane63(cum) * (double)p);
+    const unsigned long long need = target - above;    // > 0 at every level
+    int t = __ffsll((long long)__ballot(cum >= need)) - 1;
+    t = t < 0 ? 63 : t;  // unreachable: the range always holds at least `need`
+    above += readlane_u64(cum, t) - readlane_u64(mass, t);
+    prefix = level == 0 ? (uint32_t)(63 - t + 64) : (prefix << width) | (uint32_t)(63 - t);
+    wave_lds_sync();  // every lane has read the bins before the next level clears them
   }
-  const uint32_t T = lo;
-  const unsigned long long above = mass_from(T, true);
-  const unsigned long long mT = fixed_mass(T);  // > 0: S(T) > S(T + 1)
+  const uint32_t T = prefix;                    // the threshold key itself
+  const unsigned long long mT = fixed_mass(T);  // > 0: the keys equal to T carry mass
   const unsigned long long take = (target - above + mT - 1) / mT;
   // keep key > T, and the first `take` entries with key T in block order
   // (chunk, then e4, then lane, then element)
@@ -886,6 +905,7 @@ __device__ void select_row_long(const float *row, int nc, float p, int lane, uin
 // branches as in topp_kernel, each wave running select_row_long.
 __global__ __launch_bounds__(256) void topp_long_kernel(TopPArgs a) {
   __shared__ uint32_t sel_s[4][kLongChunks][64];
+  __shared__ unsigned long long bins_s[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int z = wave & 1;
@@ -901,7 +921,7 @@ __global__ __launch_bounds__(256) void topp_long_kernel(TopPArgs a) {
   uint32_t sel[kLongChunks];
 #pragma unroll
   for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
-  if (live) select_row_long(row, nc, a.p, lane, sel);
+  if (live) select_row_long(row, nc, a.p, lane, bins_s[wave], sel);
 #pragma unroll
   for (int c = 0; c < kLongChunks; ++c) sel_s[wave][c][lane] = sel[c];
   __syncthreads();
