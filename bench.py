@@ -6,11 +6,14 @@ layer on one MI355X.
 A step is one pass of the whole path over one layer's inputs, resident in
 HBM: prism_estimate (block means and energies, temperatures, scores, Top-P,
 union) followed by prism_block_sparse_attn over the resulting mask. Before
-each step a 512 MB scratch buffer is written so that the 256 MB Infinity Cache
-does not hold Q or K from the previous step. HIP events around each call (on
+each step a 512 MB scratch buffer is read so that the 256 MB Infinity Cache
+holds none of Q, K, V from the previous step. (Reading rather than writing
+it: a write would leave the cache full of dirty lines whose write-back then
+falls inside the timed region, traffic that is not the step's.) HIP events
+around each call (on
 the stream the kernels run on) time the phases; `value` is the median over the
 K timed steps of estimator + attention. The K steps run back to back between
-device synchronisations; their wall time per step (scratch writes included)
+device synchronisations; their wall time per step (scratch reads included)
 is reported too. Prints one JSON line.
 """
 from __future__ import annotations
@@ -243,10 +246,10 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    scratch = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MB
 
-    def flush():  # evict Q, K, V and the previous step's data from the Infinity Cache
-        scratch.fill_(1)
+    def flush():  # evict Q, K, V and the previous step's data from the Infinity Cache (reads only)
+        scratch.sum()
 
     for i in range(args.warmup):
         flush()

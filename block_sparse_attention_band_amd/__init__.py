@@ -37,6 +37,7 @@ class EstimatorConfig:
     causal: bool = True
     rope_layout: str = "interleaved"
     tau_mode: str = "fullspec"
+    keep_logits: bool = False  # also store the band logits in the workspace (inspection)
 
 
 def _torch():
@@ -82,7 +83,7 @@ def _cfg(cfg: EstimatorConfig, workspace=None) -> PrismCfg:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return PrismCfg(cfg.block_size, cfg.d_high, cfg.d_low, cfg.p, int(bool(cfg.causal)), _ROPE[cfg.rope_layout],
-                    _TAU[cfg.tau_mode], 0, ws_ptr, ws_bytes)
+                    _TAU[cfg.tau_mode], _abi.EST_KEEP_LOGITS if cfg.keep_logits else 0, ws_ptr, ws_bytes)
 
 
 def _stream(t) -> int:

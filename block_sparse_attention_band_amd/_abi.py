@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 3
+PRISM_ABI_VERSION = 4
 
 # prism_status_t
 OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH = range(10)
@@ -23,6 +23,7 @@ BF16, FP32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 TAU_FULLSPEC, TAU_NONE, TAU_UNIT, TAU_PERVEC = 0, 1, 2, 3
 MASK_U8, MASK_BITS = 0, 1
+EST_KEEP_LOGITS = 1
 
 
 class PrismTensor(ctypes.Structure):
@@ -46,7 +47,7 @@ class PrismCfg(ctypes.Structure):
     _fields_ = [
         ("block_size", ctypes.c_int32), ("d_high", ctypes.c_int32), ("d_low", ctypes.c_int32), ("p", ctypes.c_float),
         ("causal", ctypes.c_int32), ("rope_layout", ctypes.c_int32), ("tau_mode", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 

@@ -75,6 +75,7 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (cfg->causal != 0 && cfg->causal != 1) return PRISM_ERR_CONFIG;
   if (cfg->rope_layout != PRISM_ROPE_INTERLEAVED && cfg->rope_layout != PRISM_ROPE_HALF) return PRISM_ERR_CONFIG;
   if (cfg->tau_mode < PRISM_TAU_FULLSPEC || cfg->tau_mode > PRISM_TAU_PERVEC) return PRISM_ERR_CONFIG;
+  if (cfg->flags & ~PRISM_EST_KEEP_LOGITS) return PRISM_ERR_CONFIG;
   if (cfg->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
   if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
@@ -98,7 +99,8 @@ void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_c
   L->qsq_offset = off;  off = round_up(off + b * q->heads * nb * 16, 256);
   L->ksq_offset = off;  off = round_up(off + b * k->heads * nb * 16, 256);
   L->tau_offset = off;  off = round_up(off + b * q->heads * 32, 256);
-  L->logits_plane = prism::logit_plane(nb, cfg->causal);
+  const bool logits = nb > prism::kFusedMaxBlocks || (cfg->flags & PRISM_EST_KEEP_LOGITS);
+  L->logits_plane = logits ? prism::logit_plane(nb, cfg->causal) : 0;
   L->logits_offset = off; off = round_up(off + b * q->heads * 2 * (size_t)L->logits_plane * 4, 256);
   L->total_bytes = off;
   L->nb = nb;
@@ -227,6 +229,7 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   sc.qsq = pa.sq[0];
   sc.ksq = pa.sq[1];
   sc.pervec = cfg->tau_mode == PRISM_TAU_PERVEC;
+  sc.keep_logits = L.logits_plane > 0;
 
   prism::TopPArgs tp;
   tp.logits = sc.logits;
@@ -255,8 +258,12 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
   if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   sc.h0 = tp.h0 = 0;
   sc.nh = tp.nh = ta.hq;
-  if (prism::launch_score(sc, s) != hipSuccess) return PRISM_ERR_LAUNCH;
-  if (prism::launch_topp(tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (nb <= prism::kFusedMaxBlocks) {
+    if (prism::launch_score_topp(sc, tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  } else {
+    if (prism::launch_score(sc, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+    if (prism::launch_topp(tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  }
   return PRISM_OK;
 }
 

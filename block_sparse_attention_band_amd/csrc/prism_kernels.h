@@ -11,6 +11,7 @@ constexpr int kHeadDim = 128;
 constexpr int kBlock = 128;
 constexpr int kMaxBlocks = 8192;   // blocks per sequence (1,048,576 tokens)
 constexpr int kShortRow = 2048;    // rows up to this many blocks: register-resident selection
+constexpr int kFusedMaxBlocks = 1024;  // rows up to this many blocks: scores and selection in one kernel
 constexpr int kListCap = 2048;     // attention: key blocks compacted per pass over a mask row
 
 // One tensor [batch, seq, heads, 128], strides in elements.
@@ -67,6 +68,7 @@ struct ScoreArgs {
   int32_t causal;
   const float *qsq, *ksq;  // per-block segment energies (per-vector temperature)
   int32_t pervec;          // 1: scale logits by the per-vector band factors
+  int32_t keep_logits;     // fused kernel: also store the logits in the planes
 };
 
 struct TopPArgs {
@@ -85,6 +87,8 @@ hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s);
 hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s);
+// both at once, logits kept on chip (nb <= kFusedMaxBlocks)
+hipError_t launch_score_topp(const ScoreArgs &sc, const TopPArgs &tp, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

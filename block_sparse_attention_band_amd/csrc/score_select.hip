@@ -4,35 +4,28 @@
 //   S_z[i, :] = softmax over J(i) (j <= i when causal),
 //   M_z[i, :] = Top-P of S_z[i, :] at mass p, and M = M_high OR M_low.
 //
-// score_kernel: both branches' logits in one pass. The canonical dims split
-//   into three segments, high-only / middle / low-only; each 64 x 64 tile of
-//   (query block, key block) pairs accumulates the three segment dot products
-//   on fp32 MFMA 32x32x2 (every dim enters once), then
-//   L_high = (s0 + s1) * c_high and L_low = (s1 + s2) * c_low (the middle
-//   segment only when the bands overlap), in log2 units, go to the logit
-//   planes of the workspace.
-// topp_kernel: one wave per (row, both branches); exact and sort-free:
-//   * max, e_j = exp2(L_j - max), and integer masses m_j = e_j * 2^31
-//     (fixed point, so every sum is exact and independent of order);
-//   * a 64-bin histogram of the masses over e's exponent and top two
-//     mantissa bits (quarter octaves, monotone in e) by LDS atomics;
-//   * a wave scan over the bins from the top finds the bin b* where the
-//     cumulative mass first reaches p * Z: bins above b* are kept, bins below
-//     are dropped;
-//   * the (usually few) entries of b* are ranked exactly by (value
-//     descending, block index ascending); an entry is kept when the mass
-//     ranked before it is still short of p * Z.
-//   This is the sorted-prefix definition (shortest prefix of the descending
-//   order with mass >= p, equal scores by lower index) without a sort. A bin
-//   holding more than 64 entries is refined on the next key bits; rows that
-//   stay unresolved fall back to a bisection over the fp32 bit pattern of
-//   the threshold. The first branch's selection stays in registers; the
-//   union of both is written as the mask row (bytes or bits), zeros
-//   included.
-// topp_long_kernel: rows of more than 2048 blocks (up to 8192), which do not
-//   fit in registers: the same rule by a five-pass radix select on the key
-//   over the same fixed-point masses, the row re-read from the logit plane at
-//   every pass.
+// Selection rule (every kernel below): e_j = exp2(L_j - max), integer masses
+//   m_j = floor(e_j 2^31) (fixed point, so every sum is exact and independent
+//   of order), target ceil(p Z); the kept set is the shortest prefix of the
+//   order (e descending, block index ascending) whose mass reaches the
+//   target -- the sorted-prefix Top-P, found without a sort by a radix select
+//   on the key (the bit pattern of e, monotone in e) over 64-bin LDS
+//   histograms. The union of both branches is written as the mask row (bytes
+//   or bits), zeros included.
+//
+// score_topp_kernel (rows of at most 1024 blocks): both branches' logits of a
+//   strip of 16 query blocks on fp32 MFMA 16x16x4, kept on chip (LDS, then
+//   registers), and the selection of each row (select_row_radix).
+// score_kernel + topp_kernel (rows of 1025..2048 blocks): the logits of both
+//   branches go through the workspace's logit planes (64 x 64 tiles on fp32
+//   MFMA 32x32x2), then one wave per row and branch selects.
+// score_kernel + topp_long_kernel (rows of more than 2048 blocks, up to
+//   8192): the rows do not fit in registers; the same rule by a five-level
+//   radix select, the row re-read from the logit plane at every level.
+// In every score kernel the canonical dims split into three segments,
+//   high-only / middle / low-only, each dim entering one segment's dot
+//   product once; L_high = (s0 + s1) c_high and L_low = (s1 + s2) c_low (the
+//   middle segment only when the bands overlap), in log2 units.
 #include "prism_kernels.h"
 
 namespace prism {
@@ -122,117 +115,41 @@ __device__ __forceinline__ float wave_sum(float v) { return __uint_as_float(lane
 __device__ __forceinline__ int wave_sum_i(int v) { return (int)lane63(scan_add((uint32_t)v)); }
 __device__ __forceinline__ int wave_excl_scan_i(int v, int) { return (int)scan_add((uint32_t)v) - v; }
 
-// Top-P selection of one row held by the wave: element k of lane l is block
-// j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits (-inf when j is not
-// admissible). Returns the selection bits (bit k) of this lane.
-template <int EPL>
-__device__ uint32_t select_row(const float (&x)[EPL], float p, int lane) {
-  float mx = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) mx = fmaxf(mx, x[k]);
-  mx = wave_max(mx);
-  float ex[EPL];
-  float zl = 0.f;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    ex[k] = (x[k] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[k] - mx);
-    zl += ex[k];
-  }
-  uint32_t valid = 0;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
-  if (p >= 1.0f) return valid;
-  const float Z = wave_sum(zl);
-  const float target = p * Z;
-
-  // invariant: mass(ex >= lo) >= target > mass(ex >= hi)
-  uint32_t lo = 0u, hi = 0x3F800001u;  // every ex is <= 1.0f
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    const float tm = __uint_as_float(mid);
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) s += (ex[k] >= tm) ? ex[k] : 0.f;
-    s = wave_sum(s);
-    if (s >= target) lo = mid; else hi = mid;
-  }
-  const float T = __uint_as_float(lo);
-
-  float above = 0.f;
-  int ties = 0;
-  uint32_t sel = 0, tie = 0;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    if (ex[k] > T) { above += ex[k]; sel |= 1u << k; }
-    if (ex[k] == T && ((valid >> k) & 1u)) { tie |= 1u << k; ++ties; }
-  }
-  above = wave_sum(above);
-  ties = wave_sum_i(ties);
-  // how many of the tied entries, in ascending block order, reach the target
-  int need = 0;
-  float acc = above;
-  while (need < ties && acc < target) { acc += T; ++need; }
-  if (need >= ties) return sel | tie;
-  // rank the tied entries by block index: order is (k/4, lane, k%4)
-  int base = 0;
-#pragma unroll
-  for (int e4 = 0; e4 < EPL / 4; ++e4) {
-    const uint32_t tb = (tie >> (4 * e4)) & 0xFu;
-    const int cnt = __popc(tb);
-    int rank = base + wave_excl_scan_i(cnt, lane);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if ((tb >> m) & 1u) {
-        if (rank < need) sel |= 1u << (4 * e4 + m);
-        ++rank;
-      }
-    }
-    base += wave_sum_i(cnt);
-  }
-  return sel;
-}
-
-// per-wave LDS scratch of the histogram selection
-struct WaveHist {
-  unsigned long long bin[64];  // (count << 52) | fixed-point mass
-  uint32_t cand_key[64];       // the threshold bin's entries (value bits), ascending block order
-  uint32_t cand_keep[64];      // their selection flags
-};
-
 __device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int l) {
   const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// histogram bin of a positive e (bit pattern): quarter octaves from e = 1
-__device__ __forceinline__ int bin_of(uint32_t ebits) { return min(max(508 - (int)(ebits >> 21), 0), 63); }
-
 constexpr float kMassScale = 2147483648.0f;  // fixed point: mass = e * 2^31, e <= 1
 __device__ __forceinline__ uint32_t fixed_mass(uint32_t ebits) {
   return (uint32_t)(__uint_as_float(ebits) * kMassScale);
 }
 
-// The lanes of one wave exchange data through LDS (histogram bins,
-// candidate lists). The hardware runs a wave's LDS instructions in order; this
-// fence keeps the compiler from reordering accesses across the exchange point
-// or forwarding a lane's own earlier store to its later load.
+// The lanes of one wave exchange data through LDS (histogram bins). The
+// hardware runs a wave's LDS instructions in order; this fence keeps the
+// compiler from reordering accesses across the exchange point or forwarding
+// a lane's own earlier store to its later load.
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-// Radix state: the bin of key y is clamp(base - (y >> shift), 0, 63). Level 0
-// bins quarter octaves of e below 1 (base 508 = 4 * 127, shift 21) with every
-// smaller e in bin 63 (tail). Refining bin b* either moves the tail window
-// down so that its bin 0 is the old bin 63's top quarter octave (every bin
-// then holds exactly one value of y >> shift, except the new tail), or splits
-// b* on the next (up to) 6 key bits. Returns false when the keys of b* cannot
-// be split further (all equal) or only masses that round to 0 remain.
+// Radix state: the bin of key y is clamp(base - (y >> shift), 0, 63), so
+// larger keys fall in lower bins. Level 0 bins quarter octaves of e below 1
+// (base 508 = 4 * 127, shift 21) with every smaller e in bin 63 (tail).
+// Refining bin b* either moves the tail window down so that its bin 0 is the
+// old bin 63's top quarter octave (every bin then holds exactly one value of
+// y >> shift, except the new tail), or splits b* on the next (up to) 6 key
+// bits. Returns false when b* holds a single key value (shift 0) or, in the
+// tail, only keys whose masses are 0.
 struct Radix {
   int shift = 21, base = 508;
   bool tail = true;
   __device__ int bin(uint32_t y) const { return min(max(base - (int)(y >> shift), 0), 63); }
+  // keys of bin b: [lo(b), hi(b))
+  __device__ uint32_t hi(int b) const { return (uint32_t)(base - b + 1) << shift; }
+  __device__ uint32_t lo(int b) const { return (tail && b == 63) ? 1u : (uint32_t)(base - b) << shift; }
   __device__ bool refine(int bstar) {
     if (tail && bstar == 63) {
       base -= 63;
@@ -247,47 +164,67 @@ struct Radix {
   }
 };
 
-// One histogram pass: entries with `in` set add (1 << 52 | mass) to their
-// bin; returns the threshold bin b* (cumulative mass from the top reaches the
-// target there), adds the mass of the bins above it to `before` and returns
-// b*'s entry count in *count. At the first pass (*Z == 0) it also sets Z and
-// the target ceil(p * Z).
-struct Hist {
-  __device__ static int pass_done(WaveHist &H, int lane, float p, unsigned long long &Z, unsigned long long &target,
-                                  unsigned long long &before, uint32_t *count) {
-    wave_lds_sync();
-    const unsigned long long hv = H.bin[lane];
-    const unsigned long long mass = hv & ((1ull << 52) - 1ull);
-    const unsigned long long cum = scan_add((unsigned long long)mass);  // largest values first
-    if (Z == 0) {
-      Z = readlane_u64(cum, 63);
-      target = (unsigned long long)ceil((double)Z * (double)p);
-    }
-    const unsigned long long need = target - before;  // > 0 at every pass
-    const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
-    before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
-    *count = (uint32_t)(readlane_u64(hv, bstar) >> 52);
-    return bstar;
-  }
-};
+// Histogram of one wave in LDS: 64 bins, then one spare slot per lane that
+// takes the adds of entries outside the level's range (adds without a
+// branch).
+constexpr int kBinSlots = 128;
+__device__ __forceinline__ void clear_bins(unsigned long long *bins, int lane) { bins[lane] = 0ull; }
 
-// Top-P of one row held by the wave (element k of lane l is block
-// j = 4*l + 256*(k/4) + k%4; x[k] are log2-unit logits, -inf when j is not
-// admissible; slots k/4 >= ne4 hold no admissible block).
-// Radix select on the bit pattern of e = exp2(x - max) (monotone in e) with
-// exact fixed-point masses: each pass histograms the undecided entries into
-// 64 bins, keeps every bin above the one where the cumulative mass reaches
-// p * Z, drops every bin below, and goes on with that bin. Passes run over
-// all entries while the bin holds more than 64 of them; then its entries are
-// compacted in ascending block order (one per lane) and refined there until
-// one entry decides or the rest share one value, which are taken by block
-// index. This is the shortest prefix of the (value desc, index asc) order
-// whose mass reaches p * Z. Returns this lane's selection bits, or sets
-// *fallback when the passes cannot resolve the row.
+// Reads the wave's 64-bin histogram ((count << 52) | fixed-point mass per bin,
+// bin 0 = largest keys) and returns the threshold bin b*: the first bin,
+// from the top, where the cumulative mass reaches target - before. Adds the
+// mass of the bins above b* to `before` and returns b*'s entry count in
+// *count. At the first level (*Z == 0) it also sets Z and the target
+// ceil(p * Z).
+__device__ __forceinline__ int threshold_bin(const unsigned long long *bins, int lane, float p, unsigned long long &Z,
+                                             unsigned long long &target, unsigned long long &before, uint32_t *count) {
+  wave_lds_sync();
+  const unsigned long long hv = bins[lane];
+  const unsigned long long mass = hv & ((1ull << 52) - 1ull);
+  const unsigned long long cum = scan_add((unsigned long long)mass);  // largest values first
+  if (Z == 0) {
+    Z = readlane_u64(cum, 63);
+    target = (unsigned long long)ceil((double)Z * (double)p);
+  }
+  const unsigned long long need = target - before;  // > 0 at every level
+  const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
+  before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
+  *count = (uint32_t)(readlane_u64(hv, bstar) >> 52);
+  wave_lds_sync();  // every lane has read the bins before they are cleared again
+  return bstar;
+}
+
+// One histogram level: the keys in [lo, hi) of the admissible slots add
+// (1 << 52) | mass to their bin, the others to the lane's spare slot.
 template <int EPL>
-__device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int lane, WaveHist &H,
-                                    bool *fallback) {
-  *fallback = false;
+__device__ __forceinline__ void hist_range(const uint32_t (&key)[EPL], int ne4, uint32_t lo, uint32_t hi,
+                                           const Radix &R, unsigned long long *bins, int lane) {
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    if (k / 4 >= ne4) continue;
+    const bool in = key[k] >= lo && key[k] < hi;
+    atomicAdd(&bins[in ? R.bin(key[k]) : 64 + lane], (1ull << 52) | fixed_mass(key[k]));
+  }
+}
+
+// Top-P of one row held by the wave: element k of lane l is block
+// j = 4 l + 256 (k / 4) + k % 4; x[k] are log2-unit logits, -inf where j is
+// not admissible; slots k / 4 >= ne4 hold no admissible block. `bins` is the
+// wave's LDS histogram (kBinSlots entries). Returns this lane's selection bits.
+//
+// The rule: e_j = exp2(x_j - max), integer masses m_j = floor(e_j 2^31)
+// (fixed point: every sum exact and independent of order), target
+// ceil(p Z) with Z the sum of the masses; the selection is the shortest
+// prefix of the order (e descending, block ascending) whose mass reaches the
+// target. It is found by a radix select on the key (the bit pattern of e,
+// monotone in e): each level histograms the undecided keys into 64 bins and
+// keeps the bin b* where the mass from the top reaches the target; keys
+// above b* are kept, keys below dropped, and the next level splits b*. It
+// ends when b* holds one entry (which the target needs: every key down to
+// it is kept) or one key value (the first ceil(still needed / its mass)
+// entries with that key are kept, in block order). No sort, no fallback.
+template <int EPL>
+__device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, int lane, unsigned long long *bins) {
   float mx = -INFINITY;
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
@@ -303,14 +240,14 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
     return valid;
   }
 
-  // key = bit pattern of e (exp2(-inf) = 0 marks an entry that is not
-  // admissible; an e that underflows to 0 is never needed since p * Z <= Z).
-  // The first histogram pass runs while the keys are made.
+  // keys (exp2(-inf) = 0 marks an entry that is not admissible; an e that
+  // underflows to 0 is never needed since p * Z <= Z); the first level's
+  // histogram is made with them
   uint32_t key[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) key[k] = 0u;
   Radix R;
-  H.bin[lane] = 0ull;
+  clear_bins(bins, lane);
   wave_lds_sync();
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
@@ -319,153 +256,50 @@ __device__ uint32_t select_row_hist(const float (&x)[EPL], int ne4, float p, int
     for (int m = 0; m < 4; ++m) {
       const int k = 4 * e4 + m;
       key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
-      if (key[k]) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
+      atomicAdd(&bins[key[k] ? R.bin(key[k]) : 64 + lane], (1ull << 52) | fixed_mass(key[k]));
     }
   }
   unsigned long long Z = 0, target = 0, before = 0;
-  uint32_t sel = 0, c = 0, act = 0;
-  int bstar = 0;
-  for (int level = 0;; ++level) {
-    if (level > 0) {
-      H.bin[lane] = 0ull;
-      wave_lds_sync();
-#pragma unroll
-      for (int e4 = 0; e4 < EPL / 4; ++e4) {
-        if (e4 >= ne4) break;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int k = 4 * e4 + m;
-          if ((act >> k) & 1u) atomicAdd(&H.bin[R.bin(key[k])], (1ull << 52) | fixed_mass(key[k]));
-        }
-      }
-    }
-    bstar = Hist::pass_done(H, lane, p, Z, target, before, &c);
+  uint32_t c, lo, hi;
+  for (;;) {
+    const int bstar = threshold_bin(bins, lane, p, Z, target, before, &c);
+    lo = R.lo(bstar);
+    hi = R.hi(bstar);
+    if (c <= 1u || !R.refine(bstar)) break;
+    clear_bins(bins, lane);
     wave_lds_sync();
-    // bins above b* hold keys >= hi_key, b* holds [lo_key, hi_key) (the tail
-    // bin everything below hi_key); at level 0 every nonzero key is undecided
-    const uint32_t hi_key = (uint32_t)(R.base - bstar + 1) << R.shift;
-    const uint32_t lo_key = (R.tail && bstar == 63) ? 1u : (uint32_t)(R.base - bstar) << R.shift;
-    uint32_t nact = 0;
-#pragma unroll
-    for (int e4 = 0; e4 < EPL / 4; ++e4) {
-      if (e4 >= ne4) break;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int k = 4 * e4 + m;
-        const bool undecided = level == 0 ? key[k] != 0u : ((act >> k) & 1u) != 0u;
-        if (undecided && key[k] >= hi_key) sel |= 1u << k;
-        if (undecided && key[k] >= lo_key && key[k] < hi_key) nact |= 1u << k;
-      }
-    }
-    act = nact;
-    if (c <= 64u) break;
-    if (!R.refine(bstar)) {
-      // more than 64 undecided entries of one value: equal masses, taken
-      // by count in ascending block order (k/4, lane, k%4)
-      uint32_t kmin = ~0u, kmax = 0u;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k)
-        if ((act >> k) & 1u) { kmin = min(kmin, key[k]); kmax = max(kmax, key[k]); }
-      kmin = wave_min_u(kmin);
-      kmax = wave_max_u(kmax);
-      const unsigned long long mq = fixed_mass(kmin);
-      if (kmin != kmax || mq == 0) {
-        *fallback = true;
-        return 0;
-      }
-      const unsigned long long take = (target - before + mq - 1) / mq;  // entries needed, >= 1
-      unsigned long long rank0 = 0;
-#pragma unroll
-      for (int e4 = 0; e4 < EPL / 4; ++e4) {
-        const uint32_t nib = (act >> (4 * e4)) & 0xFu;
-        const int cnt = __popc(nib);
-        int r = (int)rank0 + wave_excl_scan_i(cnt, lane);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if ((nib >> q) & 1u) {
-            if ((unsigned long long)r < take) sel |= 1u << (4 * e4 + q);
-            ++r;
-          }
-        rank0 += (unsigned long long)wave_sum_i(cnt);
-      }
-      return sel;
-    }
-    if (level == 7) {
-      *fallback = true;
-      return 0;
-    }
+    hist_range<EPL>(key, ne4, lo, hi, R, bins, lane);
   }
-
-  // compact b*'s entries in ascending block order: slot group e4, then lane,
-  // then k % 4
-  int off[EPL / 4];
-  int total = 0;
+  uint32_t sel = 0;
+  if (c <= 1u) {  // b*'s one entry completes the mass: every key down to it is kept
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) sel |= (key[k] >= lo ? 1u : 0u) << k;
+    return sel;
+  }
+  // b* holds c > 1 entries of one key value lo: keys above it are kept, and
+  // of those equal to it the first `take` in block order (k / 4, lane, k % 4)
+  const unsigned long long mq = fixed_mass(lo);  // > 0: b* carries mass
+  const unsigned long long take = (target - before + mq - 1) / mq;
+  unsigned long long rank0 = 0;
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
-    off[e4] = 0;
-    if (e4 >= ne4) continue;
-    const uint32_t nib = (act >> (4 * e4)) & 0xFu;
-    const uint32_t cnt = __popc(nib);
-    const uint32_t incl = scan_add(cnt);
-    off[e4] = total + (int)(incl - cnt);
-    total += (int)lane63(incl);
-    int o = off[e4];
+    uint32_t nib = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if ((nib >> m) & 1u) H.cand_key[o++] = key[4 * e4 + m];
-  }
-
-  // refine on the compacted entries, one per lane
-  wave_lds_sync();
-  const uint32_t ck = lane < (int)c ? H.cand_key[lane] : 0u;
-  bool rem = lane < (int)c;  // still undecided
-  bool keep = false;
-  bool split = R.refine(bstar);
-  for (int level = 0; split && level < 8; ++level) {
-    H.bin[lane] = 0ull;
-    wave_lds_sync();
-    if (rem) atomicAdd(&H.bin[R.bin(ck)], (1ull << 52) | fixed_mass(ck));
-    uint32_t c2;
-    const int b2 = Hist::pass_done(H, lane, p, Z, target, before, &c2);
-    wave_lds_sync();
-    if (rem) {
-      const int bk = R.bin(ck);
-      keep = keep || bk < b2;
-      rem = bk == b2;
+    for (int m = 0; m < 4; ++m) {
+      const int k = 4 * e4 + m;
+      if (key[k] >= hi) sel |= 1u << k;
+      if (key[k] == lo) nib |= 1u << m;
     }
-    if (c2 == 1u) {  // that entry completes the mass
-      keep = keep || rem;
-      rem = false;
-      break;
-    }
-    split = R.refine(b2);
-  }
-  const uint64_t rb = __ballot(rem);
-  if (rb) {
-    // the undecided entries share one value: the first `take` in list order
-    const uint32_t kv = __builtin_amdgcn_readlane(ck, __ffsll((long long)rb) - 1);
-    const unsigned long long mq = fixed_mass(kv);
-    if (mq == 0) {
-      *fallback = true;
-      return 0;
-    }
-    const unsigned long long take = (target - before + mq - 1) / mq;
-    const unsigned long long r = __popcll(rb & ((1ull << lane) - 1ull));
-    keep = keep || (rem && r < take);
-  }
-  H.cand_keep[lane] = keep ? 1u : 0u;
-  wave_lds_sync();
-#pragma unroll
-  for (int e4 = 0; e4 < EPL / 4; ++e4) {
     if (e4 >= ne4) continue;
-    const uint32_t nib = (act >> (4 * e4)) & 0xFu;
-    int o = off[e4];
+    const int cnt = __popc(nib);
+    unsigned long long r = rank0 + (unsigned long long)wave_excl_scan_i(cnt, lane);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       if ((nib >> m) & 1u) {
-        if (H.cand_keep[o]) sel |= 1u << (4 * e4 + m);
-        ++o;
+        if (r < take) sel |= 1u << (4 * e4 + m);
+        ++r;
       }
+    rank0 += (unsigned long long)wave_sum_i(cnt);
   }
   return sel;
 }
@@ -718,7 +552,7 @@ __device__ void write_mask_chunk(const TopPArgs &a, int64_t row_index, int jbase
 // even wave writes the union as the mask row. Rows are taken longest first.
 template <int EPL>
 __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
-  __shared__ WaveHist whist[4];
+  __shared__ unsigned long long bins_s[4][kBinSlots];
   __shared__ uint32_t sel_s[4][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -748,17 +582,9 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
 
   uint32_t bits = 0;
   if (live) {
-    bool fallback;
-    {
-      float xr[EPL];
-      load_row(xr);
-      bits = select_row_hist<EPL>(xr, (nc + 255) / 256, a.p, lane, whist[wave], &fallback);
-    }
-    if (fallback) {
-      float xr[EPL];
-      load_row(xr);
-      bits = select_row<EPL>(xr, a.p, lane);
-    }
+    float xr[EPL];
+    load_row(xr);
+    bits = select_row_radix<EPL>(xr, (nc + 255) / 256, a.p, lane, bins_s[wave]);
   }
   sel_s[wave][lane] = bits;
   __syncthreads();
@@ -768,10 +594,219 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
   write_mask_chunk(a, (int64_t)bh * a.nb + i, 0, EPL / 4, bits, lane);
 }
 
+// ---- scores and Top-P in one kernel (rows of at most 1024 blocks)
+//
+// One workgroup (8 waves) = 16 consecutive query blocks of one head; wave w
+// owns query blocks 16 I + w and 16 I + w + 8. Two workgroups share a CU
+// (registers and LDS are sized for it), so that one's MFMA phase runs
+// beside the other's selection phase. The strip's logits are made 256 key
+// blocks at a time: wave w computes the 16 x 16 tiles w and w + 8 (key
+// blocks 256 c + 16 t .. + 15) x (the strip's 16 query blocks) on fp32 MFMA
+// 16x16x4, with A = Kbar rows (lane l: key l % 16, dims 16 m + 4 (l / 16) + e
+// of dim group m, loaded from global memory as one float4 per group) and
+// B = Qbar (the same dims of query l % 16, from LDS), so every canonical dim
+// enters once and each group of 16 dims lies in one segment (high-only,
+// middle, low-only) when the segment boundaries are multiples of 16. The
+// lane's outputs are four consecutive key blocks of one query block; both
+// branches' logits go to an LDS chunk buffer (rows padded to 260 floats, so
+// the 16 query rows of one store fall in distinct banks), and after the
+// barrier every wave reads its two rows in the selection layout (element k
+// of lane l = block 4 l + 256 (k / 4) + k % 4). The logits never leave the
+// chip. Then each wave selects its rows' branches in turn
+// (select_row_radix) and writes each row's union as its mask row.
+constexpr int kStrip = 16;             // query blocks per workgroup
+constexpr int kFusedWaves = 8;
+constexpr int kFusedChunk = 256;       // key blocks per score chunk
+constexpr int kFusedPitch = kFusedChunk + 4;
+constexpr int kRuntime16 = 100;
+
+template <int LO16, int HI16, bool PV>
+__global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void score_topp_kernel(ScoreArgs a, TopPArgs t) {
+  __shared__ __attribute__((aligned(16))) float lt[2][kStrip][kFusedPitch];  // [branch][row][key]
+  __shared__ __attribute__((aligned(16))) float4 qs[kStrip * 32];           // Qbar rows, 16-byte slots swizzled
+  __shared__ unsigned long long bins_s[kFusedWaves][kBinSlots];
+
+  const int nI = (a.nb + kStrip - 1) / kStrip;
+  const int nbh = a.batch * a.nh;
+  const int lbh = blockIdx.x % nbh;
+  const int rank = blockIdx.x / nbh;
+  const int I = a.causal ? nI - 1 - rank : rank;  // longest strips first
+  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+  const int b = bh / a.hq, h = bh % a.hq, gk = h / (a.hq / a.hkv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q0 = I * kStrip;
+  const int ncol = a.causal ? min(a.nb, q0 + kStrip) : a.nb;  // key blocks any row of the strip admits
+  const int nchunk = (ncol + kFusedChunk - 1) / kFusedChunk;
+  const int r16 = lane & 15, g4 = lane >> 4;
+
+  // the strip's Qbar rows -> LDS: row r, slot s (dims 4s..4s+3) at s ^ r
+  {
+    const int r = tid >> 5, s = tid & 31;  // 512 threads, one slot each
+    qs[r * 32 + (s ^ r)] = *reinterpret_cast<const float4 *>(
+        a.qbar + ((int64_t)bh * a.nb + min(q0 + r, a.nb - 1)) * kHeadDim + 4 * s);
+  }
+
+  const float kLog2e = 1.4426950408889634f;
+  const float *tau = a.tau + (int64_t)bh * 8;
+  const float ch = kLog2e / (tau[0] * sqrtf((float)a.d_high));
+  const float cl = kLog2e / (tau[1] * sqrtf((float)a.d_low));
+  float fqh = 1.f, fql = 1.f;  // per-vector factors of this lane's query block
+  if constexpr (PV) {
+    const float4 e = *reinterpret_cast<const float4 *>(a.qsq + ((int64_t)bh * a.nb + min(q0 + r16, a.nb - 1)) * 4);
+    fqh = pervec_factor(e, 0, a.overlap, a.d_high);
+    fql = pervec_factor(e, 1, a.overlap, a.d_low);
+  }
+  const float *kbase = a.kbar + ((int64_t)b * a.hkv + gk) * a.nb * kHeadDim;
+  const float *ksq = a.ksq + ((int64_t)b * a.hkv + gk) * a.nb * 4;
+
+  // this wave's two query blocks: r = 0 -> 16 I + w, r = 1 -> 16 I + w + 8
+  int iq[2], nc[2];
+  bool live[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    iq[r] = q0 + wave + kFusedWaves * r;
+    live[r] = iq[r] < a.nb;
+    nc[r] = a.causal ? iq[r] + 1 : a.nb;
+  }
+  float xh[2][16], xl[2][16];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) { xh[r][k] = -INFINITY; xl[r][k] = -INFINITY; }
+
+  // Kbar operands stream in half tiles (dim groups 4 hf .. 4 hf + 3, one
+  // float4 each) through two register buffers: the next half tile's loads
+  // are issued before the current one's MFMAs (across tiles and chunks too),
+  // so the load latency overlaps the MFMAs, the barriers and the row reads.
+  // Valid (chunk, tile) pairs form a prefix of the sequence.
+  auto tile_valid = [&](int c, int tt) { return c < nchunk && kFusedChunk * c + 16 * (wave + kFusedWaves * tt) < ncol; };
+  auto load_half = [&](int c, int tt, int hf, float4 (&dst)[4]) {
+    const int j = min(kFusedChunk * c + 16 * (wave + kFusedWaves * tt) + r16, a.nb - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      dst[m] = *reinterpret_cast<const float4 *>(kbase + (int64_t)j * kHeadDim + 16 * (4 * hf + m) + 4 * g4);
+  };
+  float4 kb[2][4];
+  if (tile_valid(0, 0)) load_half(0, 0, 0, kb[0]);
+
+  __syncthreads();  // Qbar in LDS
+#pragma unroll
+  for (int c = 0; c < kFusedMaxBlocks / kFusedChunk; ++c) {
+    if (c >= nchunk) break;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int tile = wave + kFusedWaves * tt;
+      const int jt = kFusedChunk * c + 16 * tile;  // first key block of the tile
+      if (!tile_valid(c, tt)) continue;
+      f32x4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int st = 4 * c + 2 * tt + hf;  // step of the sequence; buffer st % 2
+        // prefetch the next step's half tile
+        if (hf == 0) {
+          load_half(c, tt, 1, kb[(st + 1) & 1]);
+        } else if (tt == 0) {
+          if (tile_valid(c, 1)) load_half(c, 1, 0, kb[(st + 1) & 1]);
+        } else {
+          if (tile_valid(c + 1, 0)) load_half(c + 1, 0, 0, kb[(st + 1) & 1]);
+        }
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const int m = 4 * hf + mm;
+          const float4 qv4 = qs[r16 * 32 + ((4 * m + g4) ^ r16)];
+          const float qv[4] = {qv4.x, qv4.y, qv4.z, qv4.w};
+          const float4 k4 = kb[st & 1][mm];
+          const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+          if constexpr (LO16 >= 0) {
+            const int lo16 = LO16 == kRuntime16 ? a.seg_lo >> 4 : LO16;
+            const int hi16 = LO16 == kRuntime16 ? a.seg_hi >> 4 : HI16;
+            if (m < lo16) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qv[e], acc0, 0, 0, 0);
+            } else if (m < hi16) {
+              if (a.overlap) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qv[e], acc1, 0, 0, 0);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(kv[e], qv[e], acc2, 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int sd = seg_of(16 * m + 4 * g4 + e, a.seg_lo, a.seg_hi);
+              acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(sd == 0 ? kv[e] : 0.f, qv[e], acc0, 0, 0, 0);
+              acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(sd == 1 && a.overlap ? kv[e] : 0.f, qv[e], acc1, 0, 0, 0);
+              acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(sd == 2 ? kv[e] : 0.f, qv[e], acc2, 0, 0, 0);
+            }
+          }
+        }
+      }
+      // acc[r]: key block jt + 4 g4 + r against query block q0 + r16
+      f32x4v lh, ll;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float mid = a.overlap ? acc1[r] : 0.f;
+        lh[r] = (acc0[r] + mid) * ch;
+        ll[r] = (acc2[r] + mid) * cl;
+      }
+      if constexpr (PV) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 e = *reinterpret_cast<const float4 *>(ksq + (int64_t)min(jt + 4 * g4 + r, a.nb - 1) * 4);
+          lh[r] *= fqh * pervec_factor(e, 0, a.overlap, a.d_high);
+          ll[r] *= fql * pervec_factor(e, 1, a.overlap, a.d_low);
+        }
+      }
+      *reinterpret_cast<f32x4v *>(&lt[0][r16][16 * tile + 4 * g4]) = lh;
+      *reinterpret_cast<f32x4v *>(&lt[1][r16][16 * tile + 4 * g4]) = ll;
+    }
+    __syncthreads();
+    // this wave's rows, chunk c: elements 4c..4c+3 of lane l are key blocks
+    // 256 c + 4 l + e (-inf where the row does not admit them)
+    {
+      const int j = kFusedChunk * c + 4 * lane;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = wave + kFusedWaves * r;
+        const f32x4v vh = *reinterpret_cast<const f32x4v *>(&lt[0][row][4 * lane]);
+        const f32x4v vl = *reinterpret_cast<const f32x4v *>(&lt[1][row][4 * lane]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xh[r][4 * c + e] = j + e < nc[r] ? vh[e] : -INFINITY;
+          xl[r][4 * c + e] = j + e < nc[r] ? vl[e] : -INFINITY;
+        }
+        if (a.keep_logits && live[r]) {  // inspection copy in the plane layout
+          float *ph = a.logits + (int64_t)bh * 2 * a.plane + logit_row(iq[r], a.nb, a.causal);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j + e < nc[r]) {
+              ph[j + e] = vh[e];
+              ph[a.plane + j + e] = vl[e];
+            }
+        }
+      }
+    }
+    __syncthreads();  // every wave has read the chunk before the next one is stored
+  }
+
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (!live[r]) continue;
+    const int ne4 = (nc[r] + 255) / 256;
+    const uint32_t bits = select_row_radix<16>(xh[r], ne4, t.p, lane, bins_s[wave]) |
+                          select_row_radix<16>(xl[r], ne4, t.p, lane, bins_s[wave]);
+    write_mask_chunk(t, (int64_t)bh * a.nb + iq[r], 0, 4, bits, lane);
+  }
+}
+
 // Top-P of a row of more than kShortRow blocks, one wave, the row read from
 // the logit plane in chunks of 2048 blocks (element k of lane l in chunk c
 // is block 2048 c + 4 l + 256 (k / 4) + k % 4). The selection rule is
-// select_row_hist's: masses m = floor(e 2^31) of e = exp2(L - max), target
+// select_row_radix's: masses m = floor(e 2^31) of e = exp2(L - max), target
 // ceil(p Z), the shortest prefix of (e descending, block ascending) whose
 // mass reaches the target. It is found by a radix select on the key (the
 // bit pattern of e, monotone in e): five passes over the row, the first
@@ -957,11 +992,28 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_score_topp(const ScoreArgs &a, const TopPArgs &t, hipStream_t s) {
+  const dim3 grid(((a.nb + kStrip - 1) / kStrip) * a.nh * a.batch), block(kFusedWaves * 64);
+  const bool def = a.seg_lo == 32 && a.seg_hi == 64;
+  const bool by16 = a.seg_lo % 16 == 0 && a.seg_hi % 16 == 0;
+  if (a.pervec) {
+    if (def) hipLaunchKernelGGL((score_topp_kernel<2, 4, true>), grid, block, 0, s, a, t);
+    else if (by16) hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, true>), grid, block, 0, s, a, t);
+    else hipLaunchKernelGGL((score_topp_kernel<-1, -1, true>), grid, block, 0, s, a, t);
+  } else if (def) {
+    hipLaunchKernelGGL((score_topp_kernel<2, 4, false>), grid, block, 0, s, a, t);
+  } else if (by16) {
+    hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, false>), grid, block, 0, s, a, t);
+  } else {
+    hipLaunchKernelGGL((score_topp_kernel<-1, -1, false>), grid, block, 0, s, a, t);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {
   const int rows = a.batch * a.nh * a.nb;
   const dim3 grid((rows + 1) / 2);
-  if (a.nb <= 1024) hipLaunchKernelGGL((topp_kernel<16>), grid, dim3(256), 0, s, a);
-  else if (a.nb <= kShortRow) hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
+  if (a.nb <= kShortRow) hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(topp_long_kernel, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

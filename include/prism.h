@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 3
+#define PRISM_ABI_VERSION 4
 
 typedef enum {
   PRISM_OK = 0,
@@ -115,6 +115,12 @@ typedef struct {
   int32_t reserved;  /* set to 0 */
 } prism_mask_t;
 
+/* Estimator flags (prism_cfg_t.flags). KEEP_LOGITS: also store both branches'
+ * logits in the workspace (see logits_offset) for inspection. Sequences of at
+ * most 1024 blocks otherwise keep them on chip: their scores and selection
+ * run in one kernel, and the workspace has no logit planes. */
+#define PRISM_EST_KEEP_LOGITS 1
+
 typedef struct {
   int32_t block_size; /* B, tokens per block: 128 */
   int32_t d_high;     /* high-band width, even, 2..head_dim */
@@ -123,7 +129,7 @@ typedef struct {
   int32_t causal;     /* 1: query block i scores key blocks j <= i only */
   int32_t rope_layout;/* prism_rope_layout_t */
   int32_t tau_mode;   /* prism_tau_mode_t */
-  int32_t reserved;   /* set to 0 */
+  int32_t flags;      /* 0, or PRISM_EST_KEEP_LOGITS */
   void *workspace;    /* device scratch, 256-byte aligned, >= prism_estimate_workspace_bytes() */
   size_t workspace_bytes;
 } prism_cfg_t;
@@ -142,13 +148,15 @@ typedef struct {
   size_t ksq_offset;  /* fp32 [batch][Hkv][nb][4] */
   size_t tau_offset;  /* fp32 [batch][Hq][8]: tau_high, tau_low, Rq_high, Rq_low, Rq_full,
                          Rk_high, Rk_low, Rk_full */
-  size_t logits_offset; /* fp32 [batch][Hq][2][logits_plane]: branch z's (0 high, 1 low) logits
+  size_t logits_offset; /* present when logits_plane > 0 (nb > 1024, or PRISM_EST_KEEP_LOGITS):
+                         fp32 [batch][Hq][2][logits_plane]: branch z's (0 high, 1 low) logits
                          L_z[i][j] in log2 units, log2(e) Qbar_z[i].Kbar_z[j] / (tau_z sqrt(d_z)).
                          causal: packed lower triangle, row i holds j = 0..i and starts at
                          8 Q (Q + 1) + 4 R (Q + 1) floats (Q = i / 4, R = i % 4; rows padded to
                          4 floats); otherwise row i holds all nb blocks and starts at
                          i * round_up(nb, 4). */
-  int64_t logits_plane; /* floats between consecutive logit planes (a multiple of 64) */
+  int64_t logits_plane; /* floats between consecutive logit planes (a multiple of 64); 0 when
+                           the logits are not stored */
   size_t total_bytes; /* == prism_estimate_workspace_bytes() */
   int64_t nb;         /* blocks per sequence, ceil(seq / block_size) */
   int32_t seg_lo, seg_hi, overlap, reserved;
@@ -179,12 +187,14 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  *   mask_out: written in full, [batch][Hq][nb][row] in mask_out->format with
  *      nb = ceil(seq / block_size), block_size == cfg->block_size; every byte
  *      of the mask is written (0 above the diagonal when causal).
- * Work: two streaming reads of Q and K (block means and segment energies),
+ * Work: one streaming read of Q and K (block means and segment energies),
  * a per-head temperature reduction, and per query block the two band score
  * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
- * Four kernels, in order on `stream`. Rows of more than 2048 blocks are
- * selected by an exact bisection on the same fixed-point masses (one pass
- * over the row per step), giving the same selection rule.
+ * Three kernels in order on `stream` for up to 1024 blocks (scores and
+ * selection fused, logits on chip), four beyond (the logits pass through
+ * the workspace). Rows of more than 2048 blocks are selected by a radix
+ * select over the same fixed-point masses (the row re-read at each of its
+ * passes), giving the same selection rule.
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 3
+    assert lib.prism_abi_version() == 4
     for s in range(10):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
@@ -52,7 +52,7 @@ def tensor(seq=4096, heads=32, dtype=_abi.BF16, data=FAKE, head_dim=128, batch=1
 
 
 def cfg(**kw):
-    c = dict(block_size=128, d_high=64, d_low=96, p=0.95, causal=1, rope_layout=0, tau_mode=0, reserved=0,
+    c = dict(block_size=128, d_high=64, d_low=96, p=0.95, causal=1, rope_layout=0, tau_mode=0, flags=0,
              workspace=FAKE, workspace_bytes=1 << 40)
     c.update(kw)
     return PrismCfg(**c)
@@ -102,13 +102,25 @@ def test_workspace_layout(lib):
     assert L.tau_offset >= L.ksq_offset + 8 * nb * 16
     assert L.total_bytes >= L.tau_offset + 32 * 32 and L.total_bytes % 256 == 0
     assert all(o % 256 == 0 for o in (L.kbar_offset, L.qsq_offset, L.ksq_offset, L.tau_offset))
+    # up to 1024 blocks the logits stay on chip: no planes unless asked for
+    assert L.logits_plane == 0 and L.total_bytes == L.logits_offset
+    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg())) == L.total_bytes
+    keep = cfg(flags=E.EST_KEEP_LOGITS)
+    lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(keep), ctypes.byref(L))
     # logit planes: 8 blocks, causal -> rows 0..7 packed with 4-float padding = 48 floats, plane 64
     assert L.logits_plane == 64 and L.logits_offset % 256 == 0
     assert L.logits_offset >= L.tau_offset + 32 * 32
     assert L.total_bytes >= L.logits_offset + 32 * 2 * 64 * 4
-    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg())) == L.total_bytes
-    lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(causal=0)), ctypes.byref(L))
+    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(keep)) == L.total_bytes
+    lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(causal=0, flags=1)),
+                                        ctypes.byref(L))
     assert L.logits_plane == 64  # 8 rows of 8 floats
+    # unknown flag bits are rejected
+    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(flags=2))) == 0
+    # past 1024 blocks the logits always pass through the workspace
+    q2, k2 = tensor(seq=1025 * 128, heads=2), tensor(seq=1025 * 128, heads=1)
+    lib.prism_estimate_workspace_layout(ctypes.byref(q2), ctypes.byref(k2), ctypes.byref(cfg()), ctypes.byref(L))
+    assert L.nb == 1025 and L.logits_plane > 0
     # a gap between the bands: the middle segment belongs to neither
     lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(d_high=32, d_low=48)),
                                         ctypes.byref(L))

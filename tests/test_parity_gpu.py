@@ -101,7 +101,7 @@ def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=
     w = WORKLOADS[base].scaled(**over)
     say(f"[estimator] {name}: seq={w.seq} hq={w.hq} hkv={w.hkv} b={w.batch} {w.dtype} {layout} {cov}")
     q, k, _ = make_qkv(w, rope_layout=rope_layout, with_v=False)
-    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout})
+    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout, "keep_logits": check_stages})
     qd, kd = to_device(q, w.dtype, layout), to_device(k, w.dtype, layout)
     L = prism.workspace_layout(qd, kd, cfg)
     ws = torch.full((L.total_bytes,), 0xFF, dtype=torch.uint8, device="cuda")  # NaN-poisoned
@@ -109,6 +109,11 @@ def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=
     prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
     torch.cuda.synchronize()
     gm = mask.cpu().numpy()
+    if check_stages:
+        # the stored inspection copy changes nothing: same mask without it
+        plain = prism.estimate(qd, kd, cfg_of(w, **{**cov, "rope_layout": rope_layout}))
+        torch.cuda.synchronize()
+        assert np.array_equal(plain.cpu().numpy(), gm)
     orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
                                 causal=cfg.causal, rope_layout=rope_layout, tau_mode=cfg.tau_mode)
     assert set(np.unique(gm)) <= {0, 1}
