@@ -2,7 +2,7 @@
 // pipeline paragraph): block mean pooling of post-RoPE Q and K, the pooled
 // vectors' energy per band segment, and the per-head branch temperatures.
 //
-// pool_kernel: one streaming pass over Q and K. A workgroup owns one block of
+// pool_kernel: one streaming pass over Q and K. A work item is one block of
 //   B tokens for a chunk of heads of one tensor; each thread reads 16 bytes
 //   per token (8 bf16 or 4 fp32 dims), so the workgroup's loads for a token
 //   are one contiguous run when heads are adjacent in memory (BSHD); the
@@ -10,7 +10,9 @@
 //   block sum is accumulated in fp32 in token order, divided by the number
 //   of tokens present, and written in canonical frequency order (dims 2j,
 //   2j+1 = RoPE pair j). The squares of the pooled values are summed per
-//   segment (high-only, middle, low-only) for the RMS energies.
+//   segment (high-only, middle, low-only) for the RMS energies. Two
+//   persistent workgroups per CU take the work items in turn and hold their
+//   results in LDS until their reads are done.
 // tau_kernel: per query head, fixed-order fp64 sums of those segment
 //   energies over all blocks give R = sqrt(energy / (nb * |D|)) for the
 //   high band, the low band and the full spectrum of Qbar and Kbar, and
@@ -59,44 +61,58 @@ __device__ __forceinline__ uint4 ld_stream(const char *p) {
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
+// One work item = (tensor, block of B tokens, chunk of heads); this thread's
+// place in it. Lanes of a token row: TPH per head, heads of the chunk
+// adjacent; tokp token rows are read side by side.
 template <bool FP32>
-__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
+struct PoolItem {
+  static constexpr int E = Elem<FP32>::E;
+  static constexpr int TPH = kHeadDim / E;  // threads per head row
+  int ts, i, lanes_per_tok, tokp, tp, hh, dg, h;
+  bool active;
+  __device__ PoolItem(const PoolArgs &a, int item) {
+    int rem = item;
+    ts = 0;
+    const int nq = a.chunks[0] * a.nb;
+    if (rem >= nq) { ts = 1; rem -= nq; }
+    i = rem % a.nb;
+    const int chunk = rem / a.nb;
+    const int HC = a.heads_per_chunk[ts];
+    lanes_per_tok = TPH * HC;
+    tokp = kThreads / lanes_per_tok;
+    const int tid = threadIdx.x;
+    tp = tid / lanes_per_tok;
+    hh = (tid % lanes_per_tok) / TPH;
+    dg = tid % TPH;
+    h = a.h0[ts] + chunk * HC + hh;
+    active = tp < tokp && h < a.h0[ts] + a.nheads[ts];
+  }
+};
+
+// Block sums of one work item, then the mean and the segment energies of
+// this lane's dims, left in `st` (E means, then the three segment energies
+// of the head row).
+template <bool FP32>
+__device__ __forceinline__ void pool_item(const PoolArgs &a, int batch, int item, float *red, float *st) {
   using El = Elem<FP32>;
   constexpr int E = El::E;
-  constexpr int TPH = kHeadDim / E;  // threads per head row
-  __shared__ float red[kThreads * E];
-
-  const int batch = blockIdx.y;
-  int rem = blockIdx.x;
-  int ts = 0;
-  const int nq = a.chunks[0] * a.nb;
-  if (rem >= nq) { ts = 1; rem -= nq; }
-  const int i = rem % a.nb;
-  const int chunk = rem / a.nb;
-
-  const TensorArg &x = a.x[ts];
-  const int HC = a.heads_per_chunk[ts];
-  const int lanes_per_tok = TPH * HC;
-  const int tokp = kThreads / lanes_per_tok;
+  constexpr int TPH = kHeadDim / E;
+  const PoolItem<FP32> w(a, item);
+  const TensorArg &x = a.x[w.ts];
   const int tid = threadIdx.x;
-  const int tp = tid / lanes_per_tok;
-  const int hh = (tid % lanes_per_tok) / TPH;
-  const int dg = tid % TPH;
-  const int h = a.h0[ts] + chunk * HC + hh;
-  const bool active = tp < tokp && h < a.h0[ts] + a.nheads[ts];
-
-  const int t0 = i * a.block;
+  const int t0 = w.i * a.block;
   const int n = min(a.block, a.seq - t0);
 
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
-  if (active) {
+  if (w.active) {
     const char *base = static_cast<const char *>(x.data) +
-                       ((int64_t)batch * x.sb + (int64_t)h * x.sh + (int64_t)t0 * x.ss + dg * E) * El::kBytes;
+                       ((int64_t)batch * x.sb + (int64_t)w.h * x.sh + (int64_t)t0 * x.ss + w.dg * E) * El::kBytes;
     const int64_t rs = x.ss * El::kBytes;
-    int t = tp;
+    const int tokp = w.tokp;
+    int t = w.tp;
     for (; t + 7 * tokp < n; t += 8 * tokp) {
       uint4 v[8];
 #pragma unroll
@@ -108,29 +124,28 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
   }
 
   // combine the token-parallel partial sums in a fixed order
-  if (tokp > 1) {
-    if (tp < tokp) {
+  if (w.tokp > 1) {
+    if (w.tp < w.tokp) {
 #pragma unroll
       for (int e = 0; e < E; ++e) red[tid * E + e] = acc[e];
     }
     __syncthreads();
-    if (tp == 0) {
-      for (int k = 1; k < tokp; ++k) {
+    if (w.tp == 0) {
+      for (int k = 1; k < w.tokp; ++k) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] += red[(tid + k * lanes_per_tok) * E + e];
+        for (int e = 0; e < E; ++e) acc[e] += red[(tid + k * w.lanes_per_tok) * E + e];
       }
     }
   }
 
   const float inv_n = 1.0f / (float)n;
   float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-  float mean[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    mean[e] = acc[e] * inv_n;
-    const int c = dg * E + e;  // physical dim
+    st[e] = acc[e] * inv_n;
+    const int c = w.dg * E + e;  // physical dim
     const int cc = a.half_layout ? (c < kHeadDim / 2 ? 2 * c : 2 * (c - kHeadDim / 2) + 1) : c;
-    const float sq = mean[e] * mean[e];
+    const float sq = st[e] * st[e];
     if (cc < a.seg_lo) s0 += sq;
     else if (cc < a.seg_hi) s1 += sq;
     else s2 += sq;
@@ -142,23 +157,54 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
     s1 += __shfl_xor(s1, off, TPH);
     s2 += __shfl_xor(s2, off, TPH);
   }
+  st[E] = s0;
+  st[E + 1] = s1;
+  st[E + 2] = s2;
+}
 
-  if (active && tp == 0) {
-    const int64_t row = ((int64_t)batch * x.heads + h) * a.nb + i;
-    float *xb = a.xbar[ts] + row * kHeadDim;
-    if (!a.half_layout) {
+// Writes one work item's pooled row and energies from `st` (canonical order).
+template <bool FP32>
+__device__ __forceinline__ void pool_store(const PoolArgs &a, int batch, int item, const float *st) {
+  constexpr int E = Elem<FP32>::E;
+  const PoolItem<FP32> w(a, item);
+  if (!w.active || w.tp != 0) return;
+  const int64_t row = ((int64_t)batch * a.x[w.ts].heads + w.h) * a.nb + w.i;
+  float *xb = a.xbar[w.ts] + row * kHeadDim;
+  if (!a.half_layout) {
 #pragma unroll
-      for (int e = 0; e < E; e += 4)
-        *reinterpret_cast<float4 *>(xb + dg * E + e) = make_float4(mean[e], mean[e + 1], mean[e + 2], mean[e + 3]);
-    } else {
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<float4 *>(xb + w.dg * E + e) = make_float4(st[e], st[e + 1], st[e + 2], st[e + 3]);
+  } else {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int c = dg * E + e;
-        const int cc = c < kHeadDim / 2 ? 2 * c : 2 * (c - kHeadDim / 2) + 1;
-        xb[cc] = mean[e];
-      }
+    for (int e = 0; e < E; ++e) {
+      const int c = w.dg * E + e;
+      const int cc = c < kHeadDim / 2 ? 2 * c : 2 * (c - kHeadDim / 2) + 1;
+      xb[cc] = st[e];
     }
-    if (dg == 0) *reinterpret_cast<float4 *>(a.sq[ts] + row * 4) = make_float4(s0, s1, s2, 0.f);
+  }
+  if (w.dg == 0) *reinterpret_cast<float4 *>(a.sq[w.ts] + row * 4) = make_float4(st[E], st[E + 1], st[E + 2], 0.f);
+}
+
+// Persistent: workgroup g takes work items g, g + G, ... (G = gridDim.x,
+// two workgroups per CU). The results of up to kPoolSlots items wait in LDS
+// and are written after those items' reads: stores issued in the middle of
+// the read stream slow it (6.4 vs 5.9 TB/s at 128K when every workgroup's
+// items fit the slots).
+constexpr int kPoolSlots = 6;
+template <bool FP32>
+__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs a) {
+  constexpr int E = Elem<FP32>::E;
+  __shared__ float red[kThreads * E];
+  __shared__ float stash[kPoolSlots][kThreads * (E + 3)];
+  const int total = (a.chunks[0] + a.chunks[1]) * a.nb;
+  for (int first = blockIdx.x; first < total; first += kPoolSlots * gridDim.x) {
+    int nst = 0;
+    for (int item = first; item < total && nst < kPoolSlots; item += gridDim.x, ++nst) {
+      pool_item<FP32>(a, blockIdx.y, item, red, stash[nst] + threadIdx.x * (E + 3));
+      __syncthreads();  // `red` is reused by the next item
+    }
+    for (int k = 0; k < nst; ++k)
+      pool_store<FP32>(a, blockIdx.y, first + k * (int)gridDim.x, stash[k] + threadIdx.x * (E + 3));
   }
 }
 
@@ -218,7 +264,13 @@ __global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
 }  // namespace
 
 hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s) {
-  const dim3 grid((a.chunks[0] + a.chunks[1]) * a.nb, batch);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int total = (a.chunks[0] + a.chunks[1]) * a.nb;
+  const int wgs = 2 * (cus > 0 ? cus : 1);  // two resident workgroups per CU (LDS: 75 KB each)
+  const dim3 grid(total < wgs ? total : wgs, batch);
   if (fp32) hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
