@@ -202,7 +202,7 @@ __device__ __forceinline__ void hist_range(const uint32_t (&key)[EPL], int ne4, 
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
     if (k / 4 >= ne4) continue;
-    const bool in = key[k] >= lo && key[k] < hi;
+    const bool in = key[k] - lo < hi - lo;  // unsigned: lo <= key < hi
     atomicAdd(&bins[in ? R.bin(key[k]) : 64 + lane], (1ull << 52) | fixed_mass(key[k]));
   }
 }
@@ -242,7 +242,7 @@ __device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, in
 
   // keys (exp2(-inf) = 0 marks an entry that is not admissible; an e that
   // underflows to 0 is never needed since p * Z <= Z); the first level's
-  // histogram is made with them
+  // histogram is made with them, keys 0 going to the lane's spare slot.
   uint32_t key[EPL];
 #pragma unroll
   for (int k = 0; k < EPL; ++k) key[k] = 0u;
