@@ -9,7 +9,8 @@ union) followed by prism_block_sparse_attn over the resulting mask. Before
 each step a 512 MB scratch buffer is read so that the 256 MB Infinity Cache
 holds none of Q, K, V from the previous step. (Reading rather than writing
 it: a write would leave the cache full of dirty lines whose write-back then
-falls inside the timed region, traffic that is not the step's.) HIP events
+falls inside the timed region, traffic that is not the step's; the estimator
+after a written flush is reported beside the line for comparison.) HIP events
 around each call (on
 the stream the kernels run on) time the phases; `value` is the median over the
 K timed steps of estimator + attention. The K steps run back to back between
@@ -271,6 +272,19 @@ def main():
     log(f"timed: {step_ms:.3f} ms/step (median), estimator {est_ms:.3f} ms, attention {attn_ms:.3f} ms, "
         f"{wall_ms:.3f} ms/step wall incl. cache flush")
 
+    # context: the estimator after a *written* 512 MB flush, whose dirty lines are written back
+    # during the call (reported beside `value`, not in it)
+    est_w = []
+    for _ in range(args.steps):
+        scratch.fill_(1.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        prism.estimate(qd, kd, cfg, workspace=ws, mask_out=mask)
+        ev[1].record()
+        torch.cuda.synchronize()
+        est_w.append(ev[0].elapsed_time(ev[1]))
+    est_written_flush_ms = float(np.median(est_w))
+
     mask_u8 = mask
     if args.mask_bits:  # unpack (outside the timed region) for the FLOP count and the CPU baseline
         shifts = torch.arange(32, device="cuda", dtype=torch.int32)
@@ -292,6 +306,7 @@ def main():
                    "rope_theta": w.theta, "causal": True, "parallelism": "none",
                    "mask_format": "bits" if args.mask_bits else "u8"},
         "estimator_ms": round(est_ms, 3), "attention_ms": round(attn_ms, 3),
+        "estimator_ms_after_written_flush": round(est_written_flush_ms, 3),
         "wall_ms_per_step_incl_cache_flush": round(wall_ms, 3),
         "mask_density": round(density, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
