@@ -89,6 +89,9 @@ SMALL = {
     "one_block": ("llama3_8b_32k", dict(seq=100, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "fp32_iid": ("tiny_fp32_2k", dict(seq=1900, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128 - 5, hq=1, hkv=1), {}, "bshd", "interleaved"),
+    # the last length whose scores and selection run fused, and the first that goes through the planes
+    "nb_1024_fused_edge": ("llama3_8b_32k", dict(seq=1024 * 128, hq=2, hkv=1), {}, "bshd", "interleaved"),
+    "nb_1025_split_edge": ("llama3_8b_32k", dict(seq=1024 * 128 + 1, hq=2, hkv=1), {}, "bshd", "interleaved"),
     # RoPE variants (inputs only; the estimator is the same)
     "yarn": ("qwen3_8b_yarn_128k", dict(seq=5000, hq=4, hkv=1), {}, "bshd", "interleaved"),
     "mrope_video": ("qwen3_vl_8b_video_32k",
@@ -296,7 +299,7 @@ def test_attention_bit_mask_equals_byte_mask(dtype_base, over, density, causal):
 
 
 LONG = {
-    # rows longer than 2048 blocks take the bisection selection and the
+    # rows longer than 2048 blocks take the five-level radix selection (topp_long_kernel) and the
     # chunked attention block list
     "nb_4100_causal": ("llama3_8b_32k", dict(seq=4100 * 128 - 7, hq=1, hkv=1), dict()),
     "nb_2300_noncausal_p05": ("llama3_8b_32k", dict(seq=2300 * 128, hq=1, hkv=1, causal=False), dict(p=0.5)),
