@@ -346,12 +346,14 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
           sacc[t][r] = s > lim ? -INFINITY : sacc[t][r];
         }
     }
-    float mloc = -INFINITY;
+    // row max as two chains of three-input maxes (one v_max3 per two scores)
+    float ma = fmaxf(sacc[0][0], sacc[0][1]), mb = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mloc = fmaxf(mloc, fmaxf(sacc[t][r], sacc[t][r + 1]));
-    mloc = xhalf_max(mloc);
+    for (int r = 2; r < 16; r += 2) {
+      ma = __builtin_fmaxf(__builtin_fmaxf(ma, sacc[0][r]), sacc[0][r + 1]);
+      mb = __builtin_fmaxf(__builtin_fmaxf(mb, sacc[1][r]), sacc[1][r + 1]);
+    }
+    const float mloc = xhalf_max(fmaxf(ma, mb));
     // Lazy rescaling: the exponent reference m_ref only moves (and O, l are
     // rescaled) when some query's running max exceeds it by more than
     // kLazy in log2 units; until then p <= 2^kLazy, exact in fp32/bf16 range.
