@@ -10,7 +10,6 @@ namespace prism {
 constexpr int kHeadDim = 128;
 constexpr int kBlock = 128;
 constexpr int kMaxBlocks = 8192;   // blocks per sequence (1,048,576 tokens)
-constexpr int kShortRow = 2048;    // rows up to this many blocks: register-resident selection
 constexpr int kFusedMaxBlocks = 1024;  // rows up to this many blocks: scores and selection in one kernel
 constexpr int kListCap = 2048;     // attention: key blocks compacted per pass over a mask row
 

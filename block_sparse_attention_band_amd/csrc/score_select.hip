@@ -16,12 +16,10 @@
 // score_topp_kernel (rows of at most 1024 blocks): both branches' logits of a
 //   strip of 16 query blocks on fp32 MFMA 16x16x4, kept on chip (LDS, then
 //   registers), and the selection of each row (select_row_radix).
-// score_kernel + topp_kernel (rows of 1025..2048 blocks): the logits of both
+// score_kernel + topp_kernel (rows of 1025..8192 blocks): the logits of both
 //   branches go through the workspace's logit planes (64 x 64 tiles on fp32
-//   MFMA 32x32x2), then one wave per row and branch selects.
-// score_kernel + topp_long_kernel (rows of more than 2048 blocks, up to
-//   8192): the rows do not fit in registers; the same rule by a five-level
-//   radix select, the row re-read from the logit plane at every level.
+//   MFMA 32x32x2), then one wave per row and branch reads its row once into
+//   registers (32, 64 or 128 logits per lane) and selects.
 // In every score kernel the canonical dims split into three segments,
 //   high-only / middle / low-only, each dim entering one segment's dot
 //   product once; L_high = (s0 + s1) c_high and L_low = (s1 + s2) c_low (the
@@ -166,21 +164,26 @@ struct Radix {
 
 // Histogram of one wave in LDS: 64 bins, then one spare slot per lane that
 // takes the adds of entries outside the level's range (adds without a
-// branch).
+// branch). A bin word is (count << CS) | fixed-point mass: CS = 52 for rows
+// of up to 2048 entries (counts below 2^12), 50 beyond (counts up to 8192
+// below 2^14, masses up to 8192 * 2^31 = 2^44 below 2^50).
 constexpr int kBinSlots = 128;
+template <int EPL>
+constexpr int count_shift() { return EPL <= 32 ? 52 : 50; }
 __device__ __forceinline__ void clear_bins(unsigned long long *bins, int lane) { bins[lane] = 0ull; }
 
-// Reads the wave's 64-bin histogram ((count << 52) | fixed-point mass per bin,
+// Reads the wave's 64-bin histogram ((count << CS) | fixed-point mass per bin,
 // bin 0 = largest keys) and returns the threshold bin b*: the first bin,
 // from the top, where the cumulative mass reaches target - before. Adds the
 // mass of the bins above b* to `before` and returns b*'s entry count in
 // *count. At the first level (*Z == 0) it also sets Z and the target
 // ceil(p * Z).
+template <int CS>
 __device__ __forceinline__ int threshold_bin(const unsigned long long *bins, int lane, float p, unsigned long long &Z,
                                              unsigned long long &target, unsigned long long &before, uint32_t *count) {
   wave_lds_sync();
   const unsigned long long hv = bins[lane];
-  const unsigned long long mass = hv & ((1ull << 52) - 1ull);
+  const unsigned long long mass = hv & ((1ull << CS) - 1ull);
   const unsigned long long cum = scan_add((unsigned long long)mass);  // largest values first
   if (Z == 0) {
     Z = readlane_u64(cum, 63);
@@ -189,13 +192,13 @@ __device__ __forceinline__ int threshold_bin(const unsigned long long *bins, int
   const unsigned long long need = target - before;  // > 0 at every level
   const int bstar = __ffsll((long long)__ballot(cum >= need)) - 1;
   before += readlane_u64(cum, bstar) - readlane_u64(mass, bstar);
-  *count = (uint32_t)(readlane_u64(hv, bstar) >> 52);
+  *count = (uint32_t)(readlane_u64(hv, bstar) >> CS);
   wave_lds_sync();  // every lane has read the bins before they are cleared again
   return bstar;
 }
 
 // One histogram level: the keys in [lo, hi) of the admissible slots add
-// (1 << 52) | mass to their bin, the others to the lane's spare slot.
+// (1 << CS) | mass to their bin, the others to the lane's spare slot.
 template <int EPL>
 __device__ __forceinline__ void hist_range(const uint32_t (&key)[EPL], int ne4, uint32_t lo, uint32_t hi,
                                            const Radix &R, unsigned long long *bins, int lane) {
@@ -203,14 +206,16 @@ __device__ __forceinline__ void hist_range(const uint32_t (&key)[EPL], int ne4, 
   for (int k = 0; k < EPL; ++k) {
     if (k / 4 >= ne4) continue;
     const bool in = key[k] - lo < hi - lo;  // unsigned: lo <= key < hi
-    atomicAdd(&bins[in ? R.bin(key[k]) : 64 + lane], (1ull << 52) | fixed_mass(key[k]));
+    atomicAdd(&bins[in ? R.bin(key[k]) : 64 + lane], (1ull << count_shift<EPL>()) | fixed_mass(key[k]));
   }
 }
 
 // Top-P of one row held by the wave: element k of lane l is block
 // j = 4 l + 256 (k / 4) + k % 4; x[k] are log2-unit logits, -inf where j is
 // not admissible; slots k / 4 >= ne4 hold no admissible block. `bins` is the
-// wave's LDS histogram (kBinSlots entries). Returns this lane's selection bits.
+// wave's LDS histogram (kBinSlots entries). Leaves this lane's selection bits
+// in sel: bit k % 32 of word k / 32 for slot k (word c covers blocks
+// 2048 c .. 2048 c + 2047).
 //
 // The rule: e_j = exp2(x_j - max), integer masses m_j = floor(e_j 2^31)
 // (fixed point: every sum exact and independent of order), target
@@ -223,21 +228,28 @@ __device__ __forceinline__ void hist_range(const uint32_t (&key)[EPL], int ne4, 
 // ends when b* holds one entry (which the target needs: every key down to
 // it is kept) or one key value (the first ceil(still needed / its mass)
 // entries with that key are kept, in block order). No sort, no fallback.
-template <int EPL>
-__device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, int lane, unsigned long long *bins) {
+template <int EPL, int W>
+__device__ void select_row_radix_w(const float (&x)[EPL], int ne4, float p, int lane, unsigned long long *bins,
+                                   uint32_t (&sel)[W]) {
+  static_assert(W == (EPL + 31) / 32, "one selection word per 32 slots");
+  constexpr int CS = count_shift<EPL>();
+#pragma unroll
+  for (int w = 0; w < W; ++w) sel[w] = 0u;
   float mx = -INFINITY;
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
-    if (e4 >= ne4) break;
+    if (e4 >= ne4) {
+      if constexpr (EPL <= 32) break;
+      else continue;  // a compile-time trip count keeps the wide loops unrolled
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) mx = fmaxf(mx, x[4 * e4 + m]);
   }
   mx = wave_max(mx);
   if (p >= 1.0f) {
-    uint32_t valid = 0;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) valid |= (x[k] != -INFINITY ? 1u : 0u) << k;
-    return valid;
+    for (int k = 0; k < EPL; ++k) sel[k >> 5] |= (x[k] != -INFINITY ? 1u : 0u) << (k & 31);
+    return;
   }
 
   // keys (exp2(-inf) = 0 marks an entry that is not admissible; an e that
@@ -251,18 +263,21 @@ __device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, in
   wave_lds_sync();
 #pragma unroll
   for (int e4 = 0; e4 < EPL / 4; ++e4) {
-    if (e4 >= ne4) break;
+    if (e4 >= ne4) {
+      if constexpr (EPL <= 32) break;
+      else continue;  // a compile-time trip count keeps the wide loops unrolled
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int k = 4 * e4 + m;
       key[k] = __float_as_uint(__builtin_amdgcn_exp2f(x[k] - mx));
-      atomicAdd(&bins[key[k] ? R.bin(key[k]) : 64 + lane], (1ull << 52) | fixed_mass(key[k]));
+      atomicAdd(&bins[key[k] ? R.bin(key[k]) : 64 + lane], (1ull << CS) | fixed_mass(key[k]));
     }
   }
   unsigned long long Z = 0, target = 0, before = 0;
   uint32_t c, lo, hi;
   for (;;) {
-    const int bstar = threshold_bin(bins, lane, p, Z, target, before, &c);
+    const int bstar = threshold_bin<CS>(bins, lane, p, Z, target, before, &c);
     lo = R.lo(bstar);
     hi = R.hi(bstar);
     if (c <= 1u || !R.refine(bstar)) break;
@@ -270,11 +285,10 @@ __device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, in
     wave_lds_sync();
     hist_range<EPL>(key, ne4, lo, hi, R, bins, lane);
   }
-  uint32_t sel = 0;
   if (c <= 1u) {  // b*'s one entry completes the mass: every key down to it is kept
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) sel |= (key[k] >= lo ? 1u : 0u) << k;
-    return sel;
+    for (int k = 0; k < EPL; ++k) sel[k >> 5] |= (key[k] >= lo ? 1u : 0u) << (k & 31);
+    return;
   }
   // b* holds c > 1 entries of one key value lo: keys above it are kept, and
   // of those equal to it the first `take` in block order (k / 4, lane, k % 4)
@@ -287,7 +301,7 @@ __device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, in
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int k = 4 * e4 + m;
-      if (key[k] >= hi) sel |= 1u << k;
+      if (key[k] >= hi) sel[k >> 5] |= 1u << (k & 31);
       if (key[k] == lo) nib |= 1u << m;
     }
     if (e4 >= ne4) continue;
@@ -296,12 +310,19 @@ __device__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, in
 #pragma unroll
     for (int m = 0; m < 4; ++m)
       if ((nib >> m) & 1u) {
-        if (r < take) sel |= 1u << (4 * e4 + m);
+        if (r < take) sel[(4 * e4 + m) >> 5] |= 1u << ((4 * e4 + m) & 31);
         ++r;
       }
     rank0 += (unsigned long long)wave_sum_i(cnt);
   }
-  return sel;
+}
+// rows of at most 2048 entries: the selection bits as one word
+template <int EPL>
+__device__ __forceinline__ uint32_t select_row_radix(const float (&x)[EPL], int ne4, float p, int lane,
+                                                     unsigned long long *bins) {
+  uint32_t sel[1];
+  select_row_radix_w<EPL, 1>(x, ne4, p, lane, bins, sel);
+  return sel[0];
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -552,8 +573,9 @@ __device__ void write_mask_chunk(const TopPArgs &a, int64_t row_index, int jbase
 // even wave writes the union as the mask row. Rows are taken longest first.
 template <int EPL>
 __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
+  constexpr int W = EPL / 32;  // selection words per lane (2048 blocks each)
   __shared__ unsigned long long bins_s[4][kBinSlots];
-  __shared__ uint32_t sel_s[4][64];
+  __shared__ uint32_t sel_s[4][W][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int z = wave & 1;
@@ -580,18 +602,22 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
     }
   };
 
-  uint32_t bits = 0;
+  uint32_t bits[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) bits[w] = 0u;
   if (live) {
     float xr[EPL];
     load_row(xr);
-    bits = select_row_radix<EPL>(xr, (nc + 255) / 256, a.p, lane, bins_s[wave]);
+    select_row_radix_w<EPL, W>(xr, (nc + 255) / 256, a.p, lane, bins_s[wave], bits);
   }
-  sel_s[wave][lane] = bits;
+#pragma unroll
+  for (int w = 0; w < W; ++w) sel_s[wave][w][lane] = bits[w];
   __syncthreads();
   if (!live || z != 0) return;
-  bits |= sel_s[wave + 1][lane];
   // union of the branches -> mask row, zeros included
-  write_mask_chunk(a, (int64_t)bh * a.nb + i, 0, EPL / 4, bits, lane);
+#pragma unroll
+  for (int w = 0; w < W; ++w)
+    if (2048 * w < a.nb) write_mask_chunk(a, (int64_t)bh * a.nb + i, 2048 * w, 8, bits[w] | sel_s[wave + 1][w][lane], lane);
 }
 
 // ---- scores and Top-P in one kernel (rows of at most 1024 blocks)
@@ -803,169 +829,6 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   }
 }
 
-// Top-P of a row of more than kShortRow blocks, one wave, the row read from
-// the logit plane in chunks of 2048 blocks (element k of lane l in chunk c
-// is block 2048 c + 4 l + 256 (k / 4) + k % 4). The selection rule is
-// select_row_radix's: masses m = floor(e 2^31) of e = exp2(L - max), target
-// ceil(p Z), the shortest prefix of (e descending, block ascending) whose
-// mass reaches the target. It is found by a radix select on the key (the
-// bit pattern of e, monotone in e): five passes over the row, the first
-// binning the keys by octave (exponent 64..127, all smaller e in the lowest
-// bin: their masses are 0), the others by the next 6, 6, 6 and 5 mantissa
-// bits of the keys that share the prefix found so far (fixed-point masses,
-// exact in any order), each keeping the bin where the mass from the top
-// reaches the target. That gives the key T with
-// mass(key >= T) >= target > mass(key > T); every key above T is kept, and
-// of the entries with key T the first ceil((target - mass(key > T)) / m(T))
-// in block order. Keys are recomputed from the logits at every pass (the
-// row stays in L2). sel[c] receives this lane's bits of chunk c; bins is
-// the wave's 64-entry LDS histogram.
-constexpr int kLongChunks = kMaxBlocks / 2048;
-
-__device__ void select_row_long(const float *row, int nc, float p, int lane, unsigned long long *bins,
-                                uint32_t (&sel)[kLongChunks]) {
-  const int nch = (nc + 2047) / 2048;
-  // logits of elements 4 e4 .. 4 e4 + 3 of chunk c (-inf past the row)
-  auto logits4 = [&](int c, int e4, float (&x)[4]) {
-    const int j = 2048 * c + 4 * lane + 256 * e4;
-    float4 t = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-    if (j < nc) t = *reinterpret_cast<const float4 *>(row + j);
-    x[0] = t.x;
-    x[1] = (j + 1 < nc) ? t.y : -INFINITY;
-    x[2] = (j + 2 < nc) ? t.z : -INFINITY;
-    x[3] = (j + 3 < nc) ? t.w : -INFINITY;
-  };
-  float mx = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c) {
-    if (c >= nch) break;
-#pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
-      float x[4];
-      logits4(c, e4, x);
-      mx = fmaxf(fmaxf(mx, fmaxf(x[0], x[1])), fmaxf(x[2], x[3]));
-    }
-  }
-  mx = wave_max(mx);
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
-  if (p >= 1.0f) {
-#pragma unroll
-    for (int c = 0; c < kLongChunks; ++c) {
-      if (c >= nch) break;
-#pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4) {
-        float x[4];
-        logits4(c, e4, x);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) sel[c] |= (x[m] != -INFINITY ? 1u : 0u) << (4 * e4 + m);
-      }
-    }
-    return;
-  }
-  // radix levels: the exponent (octaves), then mantissa bits 22..17, 16..11,
-  // 10..5 and 4..0; exp2(-inf) = 0 marks the inadmissible entries (never
-  // counted)
-  unsigned long long target = 0, above = 0;  // above: mass of the keys above the prefix's range
-  uint32_t prefix = 0;
-#pragma unroll 1
-  for (int level = 0; level < 5; ++level) {
-    const int shift = level == 0 ? 23 : 23 - 6 * level + (level == 4 ? 1 : 0);  // 23, 17, 11, 5, 0
-    const int width = level == 0 ? 0 : (level == 4 ? 5 : 6);                    // prefix bits kept per level
-    bins[lane] = 0ull;
-    wave_lds_sync();
-#pragma unroll
-    for (int c = 0; c < kLongChunks; ++c) {
-      if (c >= nch) break;
-#pragma unroll
-      for (int e4 = 0; e4 < 8; ++e4) {
-        float x[4];
-        logits4(c, e4, x);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
-          if (k != 0u && (level == 0 || (k >> (shift + width)) == prefix)) {
-            const uint32_t bin = level == 0 ? (uint32_t)max((int)(k >> 23) - 64, 0)
-                                            : (k >> shift) & ((1u << width) - 1u);
-            atomicAdd(&bins[bin], (unsigned long long)fixed_mass(k));
-          }
-        }
-      }
-    }
-    wave_lds_sync();
-    const unsigned long long mass = bins[63 - lane];  // lane 0 holds the largest keys
-    const unsigned long long cum = scan_add(mass);     // mass of this bin and every bin above it
-    if (level == 0) target = (unsigned long long)ceil((double)lane63(cum) * (double)p);
-    const unsigned long long need = target - above;    // > 0 at every level
-    int t = __ffsll((long long)__ballot(cum >= need)) - 1;
-    t = t < 0 ? 63 : t;  // unreachable: the range always holds at least `need`
-    above += readlane_u64(cum, t) - readlane_u64(mass, t);
-    prefix = level == 0 ? (uint32_t)(63 - t + 64) : (prefix << width) | (uint32_t)(63 - t);
-    wave_lds_sync();  // every lane has read the bins before the next level clears them
-  }
-  const uint32_t T = prefix;                    // the threshold key itself
-  const unsigned long long mT = fixed_mass(T);  // > 0: the keys equal to T carry mass
-  const unsigned long long take = (target - above + mT - 1) / mT;
-  // keep key > T, and the first `take` entries with key T in block order
-  // (chunk, then e4, then lane, then element)
-  unsigned long long rank0 = 0;
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c) {
-    if (c >= nch) break;
-#pragma unroll
-    for (int e4 = 0; e4 < 8; ++e4) {
-      float x[4];
-      logits4(c, e4, x);
-      uint32_t tie = 0;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t k = __float_as_uint(__builtin_amdgcn_exp2f(x[m] - mx));
-        if (k > T) sel[c] |= 1u << (4 * e4 + m);
-        if (k == T) tie |= 1u << m;
-      }
-      const int cnt = __popc(tie);
-      unsigned long long r = rank0 + (unsigned long long)wave_excl_scan_i(cnt, lane);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if ((tie >> m) & 1u) {
-          if (r < take) sel[c] |= 1u << (4 * e4 + m);
-          ++r;
-        }
-      rank0 += (unsigned long long)wave_sum_i(cnt);
-    }
-  }
-}
-
-// Rows of more than kShortRow blocks: one workgroup = two rows x two
-// branches as in topp_kernel, each wave running select_row_long.
-__global__ __launch_bounds__(256) void topp_long_kernel(TopPArgs a) {
-  __shared__ uint32_t sel_s[4][kLongChunks][64];
-  __shared__ unsigned long long bins_s[4][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int z = wave & 1;
-  const int nbh = a.batch * a.nh;
-  const int rid = blockIdx.x * 2 + (wave >> 1);
-  const bool live = rid < nbh * a.nb;
-  const int rr = live ? rid : 0;
-  const int i = a.causal ? a.nb - 1 - rr / nbh : rr / nbh;
-  const int lbh = rr % nbh;
-  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
-  const int nc = a.causal ? i + 1 : a.nb;
-  const float *row = a.logits + ((int64_t)bh * 2 + z) * a.plane + logit_row(i, a.nb, a.causal);
-  uint32_t sel[kLongChunks];
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c) sel[c] = 0u;
-  if (live) select_row_long(row, nc, a.p, lane, bins_s[wave], sel);
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c) sel_s[wave][c][lane] = sel[c];
-  __syncthreads();
-  if (!live || z != 0) return;
-  const int nchunks = (a.nb + 2047) / 2048;  // the whole row, zeros included
-#pragma unroll
-  for (int c = 0; c < kLongChunks; ++c)
-    if (c < nchunks) write_mask_chunk(a, (int64_t)bh * a.nb + i, 2048 * c, 8, sel[c] | sel_s[wave + 1][c][lane], lane);
-}
 
 }  // namespace
 
@@ -1013,8 +876,10 @@ hipError_t launch_score_topp(const ScoreArgs &a, const TopPArgs &t, hipStream_t 
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {
   const int rows = a.batch * a.nh * a.nb;
   const dim3 grid((rows + 1) / 2);
-  if (a.nb <= kShortRow) hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(topp_long_kernel, grid, dim3(256), 0, s, a);
+  // the row in registers: 32, 64 or 128 logits per lane
+  if (a.nb <= 2048) hipLaunchKernelGGL((topp_kernel<32>), grid, dim3(256), 0, s, a);
+  else if (a.nb <= 4096) hipLaunchKernelGGL((topp_kernel<64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((topp_kernel<128>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

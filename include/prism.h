@@ -192,9 +192,8 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
  * Three kernels in order on `stream` for up to 1024 blocks (scores and
  * selection fused, logits on chip), four beyond (the logits pass through
- * the workspace). Rows of more than 2048 blocks are selected by a radix
- * select over the same fixed-point masses (the row re-read at each of its
- * passes), giving the same selection rule.
+ * the workspace). Every row, up to 8192 blocks, is selected from registers
+ * by the same radix select over fixed-point masses.
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream);

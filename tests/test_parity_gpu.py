@@ -184,6 +184,22 @@ def test_estimator_uniform_rows(p):
         assert gm[0, 0, i, : int(np.ceil(p * (i + 1) - 1e-12))].all()
 
 
+@pytest.mark.timeout(600)
+def test_estimator_uniform_long_rows():
+    """Identical blocks on rows of up to 4600 blocks: every entry of a row
+    falls in one histogram bin, so rows past 4095 blocks hold more entries
+    in a bin than a 12-bit count can (the widest selection keeps 14)."""
+    from synth import f32_to_bf16_bits
+    nb = 4600
+    x = f32_to_bf16_bits(np.ones((1, nb * 128, 1, 128), np.float32))
+    p = 0.95
+    gm, _ = _estimate_and_compare("uniform long rows", x, x, "bf16", prism.EstimatorConfig(p=p))
+    for i in (2047, 2048, 4094, 4095, 4096, nb - 1):
+        keep = int(np.ceil(p * (i + 1) - 1e-12))
+        assert gm[0, 0, i, : i + 1].sum() == keep, i
+        assert gm[0, 0, i, :keep].all(), i
+
+
 @pytest.mark.parametrize("a,p", [(1.1, 0.999), (1.3, 0.9999)])
 def test_estimator_peaked_rows_deep_tail(a, p):
     """One dominant key block and p close to 1: the threshold falls far below
@@ -299,8 +315,8 @@ def test_attention_bit_mask_equals_byte_mask(dtype_base, over, density, causal):
 
 
 LONG = {
-    # rows longer than 2048 blocks take the five-level radix selection (topp_long_kernel) and the
-    # chunked attention block list
+    # rows longer than 2048 blocks take the 64- and 128-slot register selection and the chunked
+    # attention block list
     "nb_4100_causal": ("llama3_8b_32k", dict(seq=4100 * 128 - 7, hq=1, hkv=1), dict()),
     "nb_2300_noncausal_p05": ("llama3_8b_32k", dict(seq=2300 * 128, hq=1, hkv=1, causal=False), dict(p=0.5)),
     "nb_2100_p_one": ("llama3_8b_32k", dict(seq=2100 * 128, hq=1, hkv=1), dict(p=1.0)),

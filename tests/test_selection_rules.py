@@ -4,16 +4,14 @@ step (6)): with fixed-point masses m_j = floor(e_j 2^31), e_j = 2^(x_j - max)
 and the target ceil(p Z), the kept set is the shortest prefix of the order
 (e descending, block ascending) whose mass reaches the target.
 
-Both kernels find that prefix by a radix select on the key (the bit pattern
-of e, monotone in e) instead of a sort; the two models below restate their
-level structure in numpy so the equivalence with the sorted prefix can be
-checked on the CPU (they share nothing with the kernels or the oracle):
-  * rows held in registers: 64 bins per level, level 0 in quarter octaves
-    below e = 1 with a tail bin, then the threshold bin split on the next
-    6 key bits (or the tail window moved down), until the threshold bin holds
-    one entry or one key value;
-  * long rows re-read from memory: level 0 by octave, then 6, 6, 6 and 5
-    mantissa bits, which always ends on the full key.
+The kernels find that prefix by a radix select on the key (the bit pattern
+of e, monotone in e) instead of a sort, with the row held in registers (16
+to 128 entries per lane, rows of up to 8192 blocks); the model below restates
+its level structure in numpy so the equivalence with the sorted prefix can be
+checked on the CPU (it shares nothing with the kernels or the oracle): 64
+bins per level, level 0 in quarter octaves below e = 1 with a tail bin, then
+the threshold bin split on the next 6 key bits (or the tail window moved
+down), until the threshold bin holds one entry or one key value.
 """
 import numpy as np
 import pytest
@@ -68,25 +66,6 @@ def radix_select_registers(x_log2: np.ndarray, p: float) -> np.ndarray:
     return _take_ties(key >= hi, key, m, lo, target, above)
 
 
-def radix_select_long(x_log2: np.ndarray, p: float) -> np.ndarray:
-    key, m = _keys(x_log2)
-    target = int(np.ceil(int(m.sum()) * float(np.float32(p))))
-    above, prefix = 0, 0
-    for level, (shift, width) in enumerate(((23, 0), (17, 6), (11, 6), (5, 6), (0, 5))):
-        if level == 0:
-            inr = key != 0
-            b = np.maximum((key >> 23) - 64, 0)
-        else:
-            inr = (key >> (shift + width)) == prefix
-            b = (key >> shift) & ((1 << width) - 1)
-        mass = np.bincount(b[inr], weights=m[inr], minlength=64).astype(np.int64)[::-1]  # largest keys first
-        cum = np.cumsum(mass)
-        t = int(np.argmax(cum >= target - above))
-        above += int(cum[t] - mass[t])
-        prefix = (63 - t + 64) if level == 0 else (prefix << width) | (63 - t)
-    return _take_ties(key > prefix, key, m, prefix, target, above)
-
-
 def sorted_prefix_fixed_point(x_log2: np.ndarray, p: float) -> np.ndarray:
     """The same rule by an explicit stable sort (reference for the models)."""
     x = x_log2.astype(np.float32)
@@ -101,7 +80,7 @@ def sorted_prefix_fixed_point(x_log2: np.ndarray, p: float) -> np.ndarray:
     return sel
 
 
-MODELS = [radix_select_registers, radix_select_long]
+MODELS = [radix_select_registers]
 
 
 @pytest.mark.parametrize("model", MODELS)
@@ -127,7 +106,7 @@ def test_radix_ties_taken_in_block_order(model):
 @pytest.mark.parametrize("model", MODELS)
 def test_radix_threshold_in_the_tail(model):
     """p close to 1 over a spread of 60 octaves puts the threshold below
-    2^-16 of the maximum (the register model's tail window moves down)."""
+    2^-16 of the maximum (the tail window moves down)."""
     x = np.linspace(0.0, -60.0, 300).astype(np.float32)
     for p in (0.99999, 0.9999999):
         assert np.array_equal(model(x, p), sorted_prefix_fixed_point(x, p))
