@@ -121,13 +121,17 @@ def machine_microbench():
             "gemm_bf16_8192_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1)}
 
 
-def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
+def cpu_baseline(q, k, v, mask_np, out_bits, w, budget_s=24.0):
     """The CPU oracle on a bounded sample of the same layer, extrapolated to
     ms per layer: the estimator head by head (KV group by KV group) and the
     attention on 16 query-block rows per head, head by head, each until about
-    half of `budget_s` is spent."""
+    half of `budget_s` is spent. The oracle's results are then compared with
+    the GPU's (outside the timed calls): the mask of every head it estimated,
+    under the GPU tests' mask rule, and the attention rows against the GPU's
+    sparse output `out_bits` (as stored: bf16 bits or fp32)."""
     import oracle.prism_oracle as po
     from synth import to_f64
+    from tests.parity import compare_masks
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -141,36 +145,55 @@ def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
                 break
     except OSError:
         pass
-    G = w.hq // w.hkv
-    t0 = time.perf_counter()
+    t_est = 0.0
     heads_done = 0
+    per_head = {}
+    mask_check = {}
     for g in range(w.hkv):
+        t0 = time.perf_counter()
         kbar = po.mean_pool(to_f64(k[0, :, g, :], w.dtype), w.block)
-        for h in range(g * G, (g + 1) * G):
-            po.estimate_head(to_f64(q[0, :, h, :], w.dtype), None, block=w.block, d_high=w.d_high, d_low=w.d_low,
-                             p=w.p, causal=True, kbar=kbar)
+        t_est += time.perf_counter() - t0
+        for h in range(w.hq):
+            if po.kv_head(h, w.hq, w.hkv) != g:
+                continue
+            t0 = time.perf_counter()
+            r = po.estimate_head(to_f64(q[0, :, h, :], w.dtype), None, block=w.block, d_high=w.d_high,
+                                 d_low=w.d_low, p=w.p, causal=True, kbar=kbar)
+            t_est += time.perf_counter() - t0
+            per_head[(0, h)] = r
             heads_done += 1
-        if time.perf_counter() - t0 > budget_s / 2:
+        stats = compare_masks(mask_np, per_head, w.p, True)  # untimed; frees the per-head arrays
+        per_head.clear()
+        for key in ("blocks", "mismatch", "mass_tie", "score_tie", "unexcused"):
+            mask_check[key] = mask_check.get(key, 0) + stats[key]
+        if t_est > budget_s / 2:
             break
-    t_est = time.perf_counter() - t0
     est_ms = t_est / heads_done * w.hq * 1e3
+    mask_check["heads"] = heads_done
     # attention: 16 query-block rows spread over the causal length, head after
     # head, until half the budget is spent
     nb = w.nb
     rows = sorted({min(nb - 1, max(0, (nb * f) // 16)) for f in range(16, 0, -1)}, reverse=True)
-    t1 = time.perf_counter()
+    t_attn = 0.0
     blocks_done = 0
     used = []
+    max_abs = rel_norm = 0.0
     for h in range(w.hq):
-        g = h // G
+        g = po.kv_head(h, w.hq, w.hkv)
+        t0 = time.perf_counter()
         qh, kh, vh = to_f64(q[0, :, h, :], w.dtype), to_f64(k[0, :, g, :], w.dtype), to_f64(v[0, :, g, :], w.dtype)
+        t_attn += time.perf_counter() - t0
         for i in rows:
-            po.attention_block_row(qh, kh, vh, mask_np[0, h, i], i, block=w.block, causal=True)
+            t0 = time.perf_counter()
+            oo = po.attention_block_row(qh, kh, vh, mask_np[0, h, i], i, block=w.block, causal=True)
+            t_attn += time.perf_counter() - t0
             blocks_done += int(mask_np[0, h, i, : i + 1].sum())
             used.append((h, i))
-        if time.perf_counter() - t1 > budget_s / 2:
+            og = to_f64(out_bits[0, i * w.block: min((i + 1) * w.block, w.seq), h, :], w.dtype)
+            max_abs = max(max_abs, float(np.abs(og - oo).max()))
+            rel_norm = max(rel_norm, float(np.linalg.norm(og - oo) / max(np.linalg.norm(oo), 1e-30)))
+        if t_attn > budget_s / 2:
             break
-    t_attn = time.perf_counter() - t1
     total_blocks = int(np.tril(mask_np[0]).sum())
     attn_ms = t_attn / max(1, blocks_done) * total_blocks * 1e3
     return {
@@ -181,7 +204,8 @@ def cpu_baseline(q, k, v, mask_np, w, budget_s=24.0):
                    f"layer ({w.hq} heads; {total_blocks} selected blocks over all heads) -- estimator {est_ms:.0f} ms "
                    f"+ attention {attn_ms:.0f} ms"),
         "estimator_ms": round(est_ms, 1), "attention_ms": round(attn_ms, 1),
-    }
+    }, {"mask": dict(mask_check), "attention": {"rows": len(used), "max_abs": max_abs, "rel_norm": rel_norm,
+                                                "tolerance": "max_abs <= 2e-2 and rel_norm <= 1e-2 (bf16)"}}
 
 
 def main():
@@ -285,6 +309,9 @@ def main():
         est_w.append(ev[0].elapsed_time(ev[1]))
     est_written_flush_ms = float(np.median(est_w))
 
+    # the sparse output as stored, kept on the host before the dense baselines overwrite `out`
+    out_bits = (out.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16"
+                else out.cpu().numpy()) if not args.no_cpu_baseline else None
     mask_u8 = mask
     if args.mask_bits:  # unpack (outside the timed region) for the FLOP count and the CPU baseline
         shifts = torch.arange(32, device="cuda", dtype=torch.int32)
@@ -357,7 +384,8 @@ def main():
 
     if not args.no_cpu_baseline:
         log("CPU oracle baseline (bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(q, k, v, mask_u8.cpu().numpy(), w)
+        result["cpu_baseline"], result["oracle_check"] = cpu_baseline(q, k, v, mask_u8.cpu().numpy(), out_bits, w)
+        log(f"oracle check: {result['oracle_check']}")
     print(json.dumps(result), flush=True)
 
 

@@ -13,6 +13,8 @@ using prism::kBlock;
 using prism::kHeadDim;
 using prism::kMaxBlocks;
 
+constexpr int64_t kMaxKvRowStrideBytes = int64_t(1) << 24;
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int64_t esize(int32_t dtype) { return dtype == PRISM_BF16 ? 2 : 4; }
@@ -279,6 +281,11 @@ int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, co
   if (out->batch != q->batch || out->seq != q->seq || out->heads != q->heads || out->head_dim != q->head_dim)
     return PRISM_ERR_SHAPE;
   if (!non_overlapping(out)) return PRISM_ERR_STRIDE;
+  // the bf16 kernel addresses K and V rows relative to each 64-key sub-tile
+  // in 32 bits: row strides up to 16 MiB (sequence length and batch/head
+  // strides are unrestricted)
+  if (k->stride_s * esize(k->dtype) > kMaxKvRowStrideBytes || v->stride_s * esize(v->dtype) > kMaxKvRowStrideBytes)
+    return PRISM_ERR_UNSUPPORTED;
   if (!mask || !mask->data) return PRISM_ERR_NULL;
   if (mask->causal != 0 && mask->causal != 1) return PRISM_ERR_CONFIG;
   if (mask->block_size < 1) return PRISM_ERR_SHAPE;

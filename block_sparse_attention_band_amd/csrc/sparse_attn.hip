@@ -230,12 +230,15 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  // ---- K/V of this (batch, KV head) as raw buffers; row strides in bytes
-  const int kss = (int)(a.k.ss * 2), vss = (int)(a.v.ss * 2);
+  // ---- K/V of this (batch, KV head); row strides in bytes. The raw buffer
+  // resource of a sub-tile starts at its first key row (64-bit address
+  // arithmetic), so every buffer offset stays below 64 row strides whatever
+  // the sequence length and layout (row strides up to 16 MiB, checked by the
+  // host).
+  const int64_t kss = a.k.ss * 2, vss = a.v.ss * 2;
   const char *kbase = static_cast<const char *>(a.k.data) + ((int64_t)b * a.k.sb + (int64_t)g * a.k.sh) * 2;
   const char *vbase = static_cast<const char *>(a.v.data) + ((int64_t)b * a.v.sb + (int64_t)g * a.v.sh) * 2;
-  const i32x4 krs = make_rsrc(kbase, (uint32_t)((N - 1) * kss + 256));
-  const i32x4 vrs = make_rsrc(vbase, (uint32_t)((N - 1) * vss + 256));
+  const uint32_t krec = (uint32_t)((kSub - 1) * kss + 256), vrec = (uint32_t)((kSub - 1) * vss + 256);
 
   // DMA instruction u of wave w fills LDS bytes [(NW u + w) * 1024, +1024):
   // tile rows 4(NW u + w) .. +3, lane -> (row + lane/16, slot lane%16)
@@ -243,25 +246,30 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
 #pragma unroll
   for (int u = 0; u < DPW; ++u) {
     const int row = 4 * (NW * u + wave) + (lane >> 4), slot = lane & 15;
-    kdma[u] = row * kss + (kslot(slot, row) << 4);
-    vdma[u] = row * vss + (vslot(slot, row) << 4);
+    kdma[u] = row * (int)kss + (kslot(slot, row) << 4);
+    vdma[u] = row * (int)vss + (vslot(slot, row) << 4);
   }
   auto dma_sub = [&](int n, uint8_t *Kd, uint8_t *Vd) {
     const int kv0 = (int)(__builtin_amdgcn_readfirstlane((int)blist[n >> 1]) & kBlockBits) * kBlock + (n & 1) * kSub;
+    // a sub-tile starting past the sequence end (the second half of a last
+    // block of at most 64 tokens) is never computed; its rows read row N - 1
+    const int kb0 = min(kv0, N - 1);
+    const i32x4 krs = make_rsrc(kbase + kb0 * kss, krec);
+    const i32x4 vrs = make_rsrc(vbase + kb0 * vss, vrec);
     if (kv0 + kSub <= N) {
 #pragma unroll
-      for (int u = 0; u < DPW; ++u) dma16(krs, Kd + (NW * u + wave) * 1024, kdma[u], kv0 * kss);
+      for (int u = 0; u < DPW; ++u) dma16(krs, Kd + (NW * u + wave) * 1024, kdma[u], 0);
 #pragma unroll
-      for (int u = 0; u < DPW; ++u) dma16(vrs, Vd + (NW * u + wave) * 1024, vdma[u], kv0 * vss);
+      for (int u = 0; u < DPW; ++u) dma16(vrs, Vd + (NW * u + wave) * 1024, vdma[u], 0);
     } else {
       // ragged end: rows past the sequence re-read the last row; their
       // scores are masked and their probabilities are exactly 0
 #pragma unroll
       for (int u = 0; u < DPW; ++u) {
         const int row = 4 * (NW * u + wave) + (lane >> 4), slot = lane & 15;
-        const int r = min(kv0 + row, N - 1);
-        dma16(krs, Kd + (NW * u + wave) * 1024, r * kss + (kslot(slot, row) << 4), 0);
-        dma16(vrs, Vd + (NW * u + wave) * 1024, r * vss + (vslot(slot, row) << 4), 0);
+        const int r = min(kv0 + row, N - 1) - kb0;  // 0 <= r < kSub
+        dma16(krs, Kd + (NW * u + wave) * 1024, r * (int)kss + (kslot(slot, row) << 4), 0);
+        dma16(vrs, Vd + (NW * u + wave) * 1024, r * (int)vss + (vslot(slot, row) << 4), 0);
       }
     }
   };

@@ -215,6 +215,17 @@ def union(m_high: np.ndarray, m_low: np.ndarray) -> np.ndarray:
     return (m_high.astype(bool) | m_low.astype(bool)).astype(np.uint8)
 
 
+# ------------------------------------------------------- grouped-query heads
+def kv_head(h: int, hq: int, hkv: int) -> int:
+    """KV head read by query head h under grouped-query attention: the Hq query
+    heads split into Hkv contiguous groups of G = Hq / Hkv, group g sharing KV
+    head g (h // G). This is the convention of torch's scaled_dot_product_attention
+    with enable_gqa and of repeat_interleave(K, G) along the head axis."""
+    if hq % hkv:
+        raise ValueError("Hq % Hkv != 0")
+    return h // (hq // hkv)
+
+
 # ------------------------------------------------------- steps (1)-(7) together
 def estimate_head(qh: np.ndarray, kg: np.ndarray, *, block: int, d_high: int, d_low: int, p: float,
                   causal: bool = True, rope_layout: str = "interleaved", tau_mode: str = "fullspec",
@@ -258,7 +269,6 @@ def estimate(q: np.ndarray, k: np.ndarray, *, block: int, d_high: int, d_low: in
     Hkv = k.shape[2]
     if Hq % Hkv:
         raise ValueError("Hq % Hkv != 0")
-    G = Hq // Hkv
     nb = -(-N // block)
     heads = range(Hq) if heads is None else heads
     mask = np.zeros((b, Hq, nb, nb), dtype=np.uint8)
@@ -267,7 +277,7 @@ def estimate(q: np.ndarray, k: np.ndarray, *, block: int, d_high: int, d_low: in
     kbars = {}
     for bb in range(b):
         for h in heads:
-            g = h // G
+            g = kv_head(h, Hq, Hkv)
             if (bb, g) not in kbars:
                 kbars[(bb, g)] = mean_pool(k[bb, :, g, :], block)
             r = estimate_head(q[bb, :, h, :], k[bb, :, g, :], block=block, d_high=d_high, d_low=d_low,
@@ -318,13 +328,12 @@ def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np
     """
     b, N, Hq, d = q.shape
     Hkv = k.shape[2]
-    G = Hq // Hkv
     nb = -(-N // block)
     out = np.full((b, N, Hq, v.shape[3]), np.nan)
     if rows is None:
         rows = [(bb, h, i) for bb in range(b) for h in range(Hq) for i in range(nb)]
     for bb, h, i in rows:
-        g = h // G
+        g = kv_head(h, Hq, Hkv)
         out[bb, i * block: min((i + 1) * block, N), h, :] = attention_block_row(
             q[bb, :, h, :], k[bb, :, g, :], v[bb, :, g, :], mask[bb, h, i], i, block=block, causal=causal)
     return out

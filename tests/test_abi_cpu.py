@@ -244,3 +244,35 @@ def test_layout_descriptors_bhsd_accepted_by_validation(lib):
 def test_python_binding_raises_named_error(lib):
     err = _abi.PrismError(_abi.ERR_CONFIG, "prism_estimate")
     assert "PRISM_ERR_CONFIG" in str(err) and "configuration" in str(err)
+
+
+def kv_tensor(row_bytes, seq=200_000, heads=8):
+    """bf16 K/V descriptor whose token rows are row_bytes apart (e.g. a view
+    into a fused QKV projection)"""
+    ss = row_bytes // 2
+    return PrismTensor(FAKE, _abi.BF16, 0, 1, seq, heads, 128, seq * ss, ss, 128)
+
+
+def test_attention_kv_row_stride_limit(lib):
+    """K/V rows are addressed relative to each 64-key sub-tile, so the whole
+    K/V span may pass 2 GiB and 4 GiB (a fused-QKV view of a Llama-3-8B layer,
+    12 KiB per token, spans 2 GiB past 174,762 tokens); only a per-token
+    stride above 16 MiB is refused. Accepted strides are shown by the next
+    check failing instead (a mask of the wrong size), so nothing launches."""
+    seq = 400_000
+    nb = -(-seq // 128)
+    q, o = tensor(seq=seq), tensor(seq=seq)
+    bad_mask = mask(seq=seq, nk_blocks=nb + 1)
+    for row_bytes in (12288, 1 << 16, 1 << 24):
+        kv = kv_tensor(row_bytes, seq=seq)
+        assert row_bytes * (seq - 1) >= (1 << 32)  # the span passes 4 GiB
+        assert attn(lib, q, kv, kv, bad_mask, o) == E.ERR_SHAPE, row_bytes
+    over = kv_tensor((1 << 24) + 16, seq=seq)
+    ok = kv_tensor(12288, seq=seq)
+    assert attn(lib, q, over, ok, bad_mask, o) == E.ERR_UNSUPPORTED
+    assert attn(lib, q, ok, over, bad_mask, o) == E.ERR_UNSUPPORTED
+    # fp32 K/V: the same byte limit
+    ss = ((1 << 24) + 16) // 4
+    f = PrismTensor(FAKE, _abi.FP32, 0, 1, seq, 8, 128, seq * ss, ss, 128)
+    qf, of_ = tensor(seq=seq, dtype=_abi.FP32), tensor(seq=seq, dtype=_abi.FP32)
+    assert attn(lib, qf, f, f, bad_mask, of_) == E.ERR_UNSUPPORTED

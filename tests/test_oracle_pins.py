@@ -408,6 +408,49 @@ def test_empty_row_outputs_zero():
     assert np.all(o[0, 128:] == 0) and np.abs(o[0, :128]).sum() > 0
 
 
+# ------------------------------------------- grouped-query head mapping
+def gqa_estimate_error(Hq=6, Hkv=2, N=1000, seed=12):
+    """The estimator on a GQA input against the same heads run as plain
+    multi-head attention on K repeated G times along the head axis with
+    torch.repeat_interleave (the grouping torch's attention uses). Returns the
+    number of differing mask entries plus the largest temperature difference."""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=N, hq=Hq, hkv=Hkv)
+    from synth import make_qkv, to_f64
+    q, k, _ = make_qkv(w, with_v=False)
+    q64, k64 = to_f64(q, "bf16"), to_f64(k, "bf16")
+    G = Hq // Hkv
+    k_rep = torch.from_numpy(k64).repeat_interleave(G, dim=2).numpy()
+    kw = dict(block=128, d_high=64, d_low=96, p=0.9, causal=True)
+    a = po.estimate(q64, k64, **kw)
+    b = po.estimate(q64, k_rep, **kw)
+    return int((a["mask"] != b["mask"]).sum()) + float(np.abs(a["tau"] - b["tau"]).max())
+
+
+def gqa_attention_error(Hq=6, Hkv=2, N=300, B=64, seed=13):
+    """All-blocks attention on GQA input against torch's own grouped-query
+    attention (scaled_dot_product_attention with enable_gqa), fp64 on the CPU."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, N, Hq, 128))
+    k = rng.standard_normal((1, N, Hkv, 128))
+    v = rng.standard_normal((1, N, Hkv, 128))
+    nb = -(-N // B)
+    mask = np.ones((1, Hq, nb, nb), np.uint8)
+    o = po.block_sparse_attention(q, k, v, mask, block=B, causal=True)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True)
+    return float(np.abs(o - ref.permute(0, 2, 1, 3).numpy()).max())
+
+
+def test_gqa_mapping_estimate_matches_repeated_kv():
+    assert gqa_estimate_error() == 0
+    assert gqa_estimate_error(Hq=8, Hkv=2) == 0
+
+
+def test_gqa_mapping_attention_matches_torch_gqa():
+    assert gqa_attention_error() < 1e-12
+    assert gqa_attention_error(Hq=8, Hkv=4) < 1e-12
+
+
 # --------------------------------------------- planted mistakes must be caught
 def test_planted_swapped_bands_caught(monkeypatch):
     good = po.band_dims
@@ -487,3 +530,10 @@ def test_planted_wrong_pool_divisor_caught(monkeypatch):
     monkeypatch.setattr(po, "mean_pool", pool_by_B)
     # a ragged last block (139 = 8*16 + 11) exposes the wrong divisor
     assert plain_pooled_error(True) > 0
+
+
+def test_planted_interleaved_gqa_mapping_caught(monkeypatch):
+    # query head h reading KV head h % Hkv instead of h // G
+    monkeypatch.setattr(po, "kv_head", lambda h, hq, hkv: h % hkv)
+    assert gqa_estimate_error() > 0
+    assert gqa_attention_error() > 1e-3
