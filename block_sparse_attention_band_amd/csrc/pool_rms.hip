@@ -265,8 +265,8 @@ __global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
 
 hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s) {
   int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  hipError_t e = stream_device(s, &dev);
+  if (e == hipSuccess) e = device_cu_count(dev, &cus);
   if (e != hipSuccess) return e;
   const int total = (a.chunks[0] + a.chunks[1]) * a.nb;
   const int wgs = 2 * (cus > 0 ? cus : 1);  // two resident workgroups per CU (LDS: 75 KB each)

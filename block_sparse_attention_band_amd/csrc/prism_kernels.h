@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "prism.h"
+
 namespace prism {
 
 constexpr int kHeadDim = 128;
@@ -102,5 +104,20 @@ struct AttnArgs {
 
 hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------- host helpers
+// The estimator's host side, shared by the entry points that take a caller
+// workspace and the one that uses the library's own scratch: every check but
+// the workspace's (fills *L; PRISM_OK or the status), then the launches.
+int check_estimate_call(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                        const prism_mask_t *mask_out, prism_workspace_layout_t *L);
+int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                     const prism_mask_t *mask_out, const prism_workspace_layout_t &L, void *workspace,
+                     hipStream_t s);
+
+// The device a stream belongs to (the current device for the null stream).
+hipError_t stream_device(hipStream_t s, int *dev);
+// Compute units of a device, queried once per device and cached.
+hipError_t device_cu_count(int dev, int *cus);
 
 }  // namespace prism
