@@ -18,8 +18,8 @@ from dataclasses import dataclass
 from . import _abi
 from ._abi import PrismCfg, PrismError, PrismMask, PrismTensor, PrismWorkspaceLayout, lib
 
-__all__ = ["EstimatorConfig", "estimate", "block_sparse_attn", "workspace_bytes", "workspace_layout",
-           "PrismError", "lib"]
+__all__ = ["EstimatorConfig", "estimate", "estimate_noalloc", "block_sparse_attn", "workspace_bytes",
+           "workspace_layout", "PrismError", "lib"]
 
 _ROPE = {"interleaved": _abi.ROPE_INTERLEAVED, "half": _abi.ROPE_HALF}
 _TAU = {"fullspec": _abi.TAU_FULLSPEC, "none": _abi.TAU_NONE, "unit": _abi.TAU_UNIT,
@@ -127,6 +127,22 @@ def estimate(q, k, cfg: EstimatorConfig = EstimatorConfig(), *, workspace=None, 
     md = mask_desc(mask_out, cfg.block_size, cfg.causal)
     _abi.check(lib().prism_estimate(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(c), ctypes.byref(md),
                                     ctypes.c_void_p(_stream(q))), "prism_estimate")
+    return mask_out
+
+
+def estimate_noalloc(q, k, cfg: EstimatorConfig = EstimatorConfig(), *, mask_out=None, bits: bool = False):
+    """prism_estimate_noalloc: the same mask as estimate(), with the library's own device
+    scratch as the workspace (no workspace argument; nothing allocated by the library).
+    A mask_out given by the caller makes the call allocation-free end to end."""
+    torch = _torch()
+    if mask_out is None:
+        nb = (q.shape[1] + cfg.block_size - 1) // cfg.block_size
+        shape = (q.shape[0], q.shape[2], nb, (nb + 31) // 32 if bits else nb)
+        mask_out = torch.empty(shape, dtype=torch.int32 if bits else torch.uint8, device=q.device)
+    qd, kd, c = tensor_desc(q), tensor_desc(k), _cfg(cfg)
+    md = mask_desc(mask_out, cfg.block_size, cfg.causal)
+    _abi.check(lib().prism_estimate_noalloc(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(c), ctypes.byref(md),
+                                            ctypes.c_void_p(_stream(q))), "prism_estimate_noalloc")
     return mask_out
 
 

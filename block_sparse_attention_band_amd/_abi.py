@@ -12,13 +12,15 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 4
+PRISM_ABI_VERSION = 5
 
 # prism_status_t
-OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH = range(10)
+(OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH,
+ ERR_SCRATCH) = range(11)
 STATUS_NAMES = ["PRISM_OK", "PRISM_ERR_NULL", "PRISM_ERR_DTYPE", "PRISM_ERR_SHAPE", "PRISM_ERR_STRIDE",
                 "PRISM_ERR_ALIGN", "PRISM_ERR_CONFIG", "PRISM_ERR_WORKSPACE", "PRISM_ERR_UNSUPPORTED",
-                "PRISM_ERR_LAUNCH"]
+                "PRISM_ERR_LAUNCH", "PRISM_ERR_SCRATCH"]
+NOALLOC_SCRATCH_BYTES = 40 << 20
 BF16, FP32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 TAU_FULLSPEC, TAU_NONE, TAU_UNIT, TAU_PERVEC = 0, 1, 2, 3
@@ -71,6 +73,9 @@ SIGNATURES = [
      [ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismCfg),
       ctypes.POINTER(PrismWorkspaceLayout)]),
     ("prism_estimate", ctypes.c_int,
+     [ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismCfg),
+      ctypes.POINTER(PrismMask), ctypes.c_void_p]),
+    ("prism_estimate_noalloc", ctypes.c_int,
      [ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismTensor), ctypes.POINTER(PrismCfg),
       ctypes.POINTER(PrismMask), ctypes.c_void_p]),
     ("prism_block_sparse_attn", ctypes.c_int,

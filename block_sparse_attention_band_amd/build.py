@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libprism.so")
 
-SOURCES = ["prism_abi.cpp", "device_info.cpp", "pool_rms.hip", "score_select.hip", "sparse_attn.hip"]
+SOURCES = ["prism_abi.cpp", "device_info.cpp", "pool_rms.hip", "score_select.hip", "sparse_attn.hip", "noalloc.hip"]
 # Scores in these kernels are finite or -inf, never NaN: without NaN semantics
 # fmax needs no canonicalising v_max per operand (a third of the softmax VALU).
 EXTRA = {"score_select.hip": ["-fno-honor-nans"], "sparse_attn.hip": ["-fno-honor-nans"]}

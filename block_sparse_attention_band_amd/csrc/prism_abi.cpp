@@ -148,6 +148,7 @@ const char *prism_status_str(int status) {
     case PRISM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PRISM_ERR_UNSUPPORTED: return "unsupported size or setting";
     case PRISM_ERR_LAUNCH: return "kernel launch failed";
+    case PRISM_ERR_SCRATCH: return "problem needs more workspace than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -167,24 +168,28 @@ size_t prism_estimate_workspace_bytes(const prism_tensor_t *q, const prism_tenso
   return L.total_bytes;
 }
 
-int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
-                   prism_mask_t *mask_out, void *stream) {
+}  // extern "C"
+
+namespace prism {
+
+int check_estimate_call(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                        const prism_mask_t *mask_out, prism_workspace_layout_t *L) {
   int st = check_estimate_args(q, k, cfg);
   if (st) return st;
-  prism_workspace_layout_t L;
-  make_layout(q, k, cfg, &L);
-  if (!cfg->workspace || reinterpret_cast<uintptr_t>(cfg->workspace) % 256 || cfg->workspace_bytes < L.total_bytes)
-    return PRISM_ERR_WORKSPACE;
+  make_layout(q, k, cfg, L);
   if (!mask_out || !mask_out->data) return PRISM_ERR_NULL;
-  if (mask_out->batch != q->batch || mask_out->heads != q->heads || mask_out->nq_blocks != L.nb ||
-      mask_out->nk_blocks != L.nb || mask_out->block_size != cfg->block_size)
+  if (mask_out->batch != q->batch || mask_out->heads != q->heads || mask_out->nq_blocks != L->nb ||
+      mask_out->nk_blocks != L->nb || mask_out->block_size != cfg->block_size)
     return PRISM_ERR_SHAPE;
-  if ((st = check_mask_format(mask_out))) return st;
+  return check_mask_format(mask_out);
+}
 
-  char *ws = static_cast<char *>(cfg->workspace);
+int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                     const prism_mask_t *mask_out, const prism_workspace_layout_t &L, void *workspace,
+                     hipStream_t s) {
+  char *ws = static_cast<char *>(workspace);
   const int fp32 = q->dtype == PRISM_FP32;
   const int nb = (int)L.nb;
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   prism::PoolArgs pa;
   const prism_tensor_t *xs[2] = {q, k};
@@ -267,6 +272,20 @@ int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism
     if (prism::launch_topp(tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   }
   return PRISM_OK;
+}
+
+}  // namespace prism
+
+extern "C" {
+
+int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                   prism_mask_t *mask_out, void *stream) {
+  prism_workspace_layout_t L;
+  const int st = prism::check_estimate_call(q, k, cfg, mask_out, &L);
+  if (st) return st;
+  if (!cfg->workspace || reinterpret_cast<uintptr_t>(cfg->workspace) % 256 || cfg->workspace_bytes < L.total_bytes)
+    return PRISM_ERR_WORKSPACE;
+  return prism::enqueue_estimate(q, k, cfg, mask_out, L, cfg->workspace, static_cast<hipStream_t>(stream));
 }
 
 int prism_block_sparse_attn(const prism_tensor_t *q, const prism_tensor_t *k, const prism_tensor_t *v,

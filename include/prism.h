@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 4
+#define PRISM_ABI_VERSION 5
 
 typedef enum {
   PRISM_OK = 0,
@@ -61,7 +61,9 @@ typedef enum {
   PRISM_ERR_CONFIG = 6,      /* d_high, d_low, p, rope_layout or tau_mode out of range */
   PRISM_ERR_WORKSPACE = 7,   /* workspace NULL, not 256-byte aligned, or too small */
   PRISM_ERR_UNSUPPORTED = 8, /* valid but not built: head_dim != 128, block != 128, too many blocks */
-  PRISM_ERR_LAUNCH = 9       /* a kernel launch failed */
+  PRISM_ERR_LAUNCH = 9,      /* a kernel launch failed */
+  PRISM_ERR_SCRATCH = 10     /* prism_estimate_noalloc: the problem needs more workspace than
+                                PRISM_NOALLOC_SCRATCH_BYTES */
 } prism_status_t;
 
 typedef enum { PRISM_BF16 = 0, PRISM_FP32 = 1 } prism_dtype_t;
@@ -199,6 +201,26 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
                    prism_mask_t *mask_out, void *stream);
+
+/* Bytes of the device array prism_estimate_noalloc uses as its workspace
+ * (40 MiB: the 131,072-token Llama-3-8B layer needs 22 MB, the 64-query-head
+ * share of a Llama-3-70B layer at the same length 37 MiB). */
+#define PRISM_NOALLOC_SCRATCH_BYTES (40u << 20)
+
+/* prism_estimate for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, checks, kernels and results as prism_estimate, except that
+ * cfg->workspace and cfg->workspace_bytes are ignored: the workspace is a
+ * device array of PRISM_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * device (held from the library's first use on that device until the process
+ * ends; the stream's device is used). The call allocates nothing. Problems
+ * whose workspace (prism_estimate_workspace_bytes) exceeds that size return
+ * PRISM_ERR_SCRATCH with nothing enqueued. Every call on a device shares that
+ * device's array, so calls that overlap on one device race (one stream, or
+ * calls ordered by the caller, per device); the workspace intermediates are
+ * not readable by the caller. */
+int prism_estimate_noalloc(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,
+                           prism_mask_t *mask_out, void *stream);
 
 /* Causal block-sparse attention prefill (abstract; gist.science Technical
  * Summary section 1): for query t of query block i and head h,

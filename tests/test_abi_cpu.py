@@ -37,8 +37,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 4
-    for s in range(10):
+    assert lib.prism_abi_version() == 5
+    for s in range(11):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
 
@@ -276,3 +276,48 @@ def test_attention_kv_row_stride_limit(lib):
     f = PrismTensor(FAKE, _abi.FP32, 0, 1, seq, 8, 128, seq * ss, ss, 128)
     qf, of_ = tensor(seq=seq, dtype=_abi.FP32), tensor(seq=seq, dtype=_abi.FP32)
     assert attn(lib, qf, f, f, bad_mask, of_) == E.ERR_UNSUPPORTED
+
+
+def noalloc(lib, q, k, c, m):
+    r = lambda x: ctypes.byref(x) if x is not None else None
+    return lib.prism_estimate_noalloc(r(q), r(k), r(c), r(m), None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(q=None), E.ERR_NULL),
+    (dict(m=mask(data=0)), E.ERR_NULL),
+    (dict(k=tensor(heads=6)), E.ERR_SHAPE),
+    (dict(c=cfg(p=1.5)), E.ERR_CONFIG),
+    (dict(m=mask(nq_blocks=31)), E.ERR_SHAPE),
+    (dict(q=tensor(head_dim=64), k=tensor(heads=8, head_dim=64)), E.ERR_UNSUPPORTED),
+])
+def test_noalloc_rejects_like_estimate(lib, case, expect):
+    """the no-allocation entry point runs the same argument checks, before any HIP call"""
+    args = dict(q=tensor(), k=tensor(heads=8), c=cfg(workspace=0, workspace_bytes=0), m=mask())
+    args.update(case)
+    assert noalloc(lib, args["q"], args["k"], args["c"], args["m"]) == expect
+    args["c"] = cfg() if args["c"] is not None and case.get("c") is None else args["c"]
+    assert est(lib, args["q"], args["k"], args["c"], args["m"]) == expect
+
+
+def test_noalloc_scratch_limit(lib):
+    """problems whose workspace exceeds PRISM_NOALLOC_SCRATCH_BYTES are refused
+    with PRISM_ERR_SCRATCH before any HIP call; the limit matches the header"""
+    src = open(HEADER).read()
+    assert "#define PRISM_NOALLOC_SCRATCH_BYTES (40u << 20)" in src
+    limit = _abi.NOALLOC_SCRATCH_BYTES
+    assert limit == 40 << 20
+    # the 64-query-head, 8-KV-head layer at 131,072 tokens fits (37 MiB) ...
+    q, k = tensor(seq=131072, heads=64), tensor(seq=131072, heads=8)
+    need = lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg()))
+    assert 36 << 20 < need <= limit
+    # ... with 80 query heads it does not
+    q2 = tensor(seq=131072, heads=80)
+    need2 = lib.prism_estimate_workspace_bytes(ctypes.byref(q2), ctypes.byref(k), ctypes.byref(cfg()))
+    assert need2 > limit
+    assert noalloc(lib, q2, k, cfg(workspace=0), mask(seq=131072, heads=80)) == E.ERR_SCRATCH
+    # past 1024 blocks the logit planes alone exceed it
+    q3, k3 = tensor(seq=2048 * 128, heads=32), tensor(seq=2048 * 128, heads=8)
+    assert noalloc(lib, q3, k3, cfg(workspace=0), mask(seq=2048 * 128)) == E.ERR_SCRATCH
+    # the inspection copy of the logits counts too
+    assert noalloc(lib, q, k, cfg(workspace=0, flags=E.EST_KEEP_LOGITS), mask(seq=131072, heads=64)) == E.ERR_SCRATCH
