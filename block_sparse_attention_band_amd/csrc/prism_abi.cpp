@@ -14,6 +14,9 @@ using prism::kHeadDim;
 using prism::kMaxBlocks;
 
 constexpr int64_t kMaxKvRowStrideBytes = int64_t(1) << 24;
+constexpr int64_t kMaxBatch = 65535;                                   // a grid dimension of the estimator
+constexpr int64_t kMaxExtent = int64_t(kMaxBlocks) * kBlock;           // 2^20 tokens, heads or batch x heads
+constexpr int64_t kMaxStride = int64_t(1) << 40;                      // elements
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -24,9 +27,14 @@ int check_tensor(const prism_tensor_t *t) {
   if (!t || !t->data) return PRISM_ERR_NULL;
   if (t->dtype != PRISM_BF16 && t->dtype != PRISM_FP32) return PRISM_ERR_DTYPE;
   if (t->batch < 1 || t->seq < 1 || t->heads < 1 || t->head_dim < 1) return PRISM_ERR_SHAPE;
-  if (t->heads * t->batch > (1 << 20)) return PRISM_ERR_UNSUPPORTED;  // grid size limit
+  // Every extent and stride is bounded before any product is formed, so no
+  // size arithmetic below (or in the layout) can overflow: batch < 2^16,
+  // heads and seq <= 2^20, strides <= 2^40 elements.
+  if (t->batch > kMaxBatch || t->heads > kMaxExtent || t->seq > kMaxExtent || t->head_dim != kHeadDim)
+    return PRISM_ERR_UNSUPPORTED;
+  if (t->heads * t->batch > kMaxExtent) return PRISM_ERR_UNSUPPORTED;  // grid size limit
   if (t->stride_b < 1 || t->stride_s < 1 || t->stride_h < 1) return PRISM_ERR_STRIDE;
-  if (t->head_dim != kHeadDim) return PRISM_ERR_UNSUPPORTED;
+  if (t->stride_b > kMaxStride || t->stride_s > kMaxStride || t->stride_h > kMaxStride) return PRISM_ERR_UNSUPPORTED;
   const int64_t es = esize(t->dtype);
   if (reinterpret_cast<uintptr_t>(t->data) % 16) return PRISM_ERR_ALIGN;
   if ((t->stride_b * es) % 16 || (t->stride_s * es) % 16 || (t->stride_h * es) % 16) return PRISM_ERR_ALIGN;

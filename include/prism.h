@@ -35,9 +35,10 @@
  *     to a million tokens is the pages' stated future work, Prism review,
  *     limitations paragraph). Launch limits: batch <= 65535 and
  *     batch * query heads * blocks * 512 < 2^32; larger problems return
- *     PRISM_ERR_UNSUPPORTED (split them by batch or head). Attention: the
- *     seq strides of k and v may span at most 16 MiB (16,777,216 bytes) per
- *     token; the tensors themselves may span any size (64-bit addressing).
+ *     PRISM_ERR_UNSUPPORTED (split them by batch or head); so do strides
+ *     above 2^40 elements. Attention: the seq strides of k and v may span at
+ *     most 16 MiB (16,777,216 bytes) per token; the tensors themselves may
+ *     span any size (64-bit addressing).
  */
 #ifndef PRISM_H
 #define PRISM_H

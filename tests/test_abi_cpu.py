@@ -250,7 +250,7 @@ def kv_tensor(row_bytes, seq=200_000, heads=8):
     """bf16 K/V descriptor whose token rows are row_bytes apart (e.g. a view
     into a fused QKV projection)"""
     ss = row_bytes // 2
-    return PrismTensor(FAKE, _abi.BF16, 0, 1, seq, heads, 128, seq * ss, ss, 128)
+    return PrismTensor(FAKE, _abi.BF16, 0, 1, seq, heads, 128, ss, ss, 128)  # batch 1: any batch stride
 
 
 def test_attention_kv_row_stride_limit(lib):
@@ -273,7 +273,7 @@ def test_attention_kv_row_stride_limit(lib):
     assert attn(lib, q, ok, over, bad_mask, o) == E.ERR_UNSUPPORTED
     # fp32 K/V: the same byte limit
     ss = ((1 << 24) + 16) // 4
-    f = PrismTensor(FAKE, _abi.FP32, 0, 1, seq, 8, 128, seq * ss, ss, 128)
+    f = PrismTensor(FAKE, _abi.FP32, 0, 1, seq, 8, 128, ss, ss, 128)
     qf, of_ = tensor(seq=seq, dtype=_abi.FP32), tensor(seq=seq, dtype=_abi.FP32)
     assert attn(lib, qf, f, f, bad_mask, of_) == E.ERR_UNSUPPORTED
 
