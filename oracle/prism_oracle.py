@@ -34,6 +34,19 @@ GPU reads. Readings taken where the pages are silent:
     highest scores whose mass reaches p (inclusive), ties by lower index;
   * attention scale 1/sqrt(d); a query with no admissible key outputs 0;
   * a partial last block averages the tokens it holds.
+The pages list two weaknesses without giving the remedy (Prism review,
+weaknesses paragraph): the static band split and the union's over-selection.
+The variants built for comparison, each a reading:
+  * adaptive split: each head's high band ends at the smallest multiple of 8
+    RoPE pairs at which the head's share of pooled spectral energy (the
+    per-pair energy of Qbar times that of Kbar, fastest pair first) reaches
+    the share the static high band holds in the mean spectrum of all query
+    heads; the low band keeps the static overlap (so d_high + d_low is
+    unchanged), and a layer whose heads share one spectrum gets the static
+    split back;
+  * merges: intersection (M_high AND M_low), and a weighted merge, one Top-P
+    on the equal-weight mixture (S_high + S_low) / 2 of the two branches'
+    block distributions.
 """
 from __future__ import annotations
 
@@ -41,6 +54,8 @@ import numpy as np
 
 ROPE_LAYOUTS = ("interleaved", "half")
 TAU_MODES = ("fullspec", "none", "unit", "pervec")
+MERGES = ("union", "intersect", "mix")
+BAND_MODES = ("static", "adaptive")
 
 
 # ---------------------------------------------------------------- step (1)
@@ -215,6 +230,84 @@ def union(m_high: np.ndarray, m_low: np.ndarray) -> np.ndarray:
     return (m_high.astype(bool) | m_low.astype(bool)).astype(np.uint8)
 
 
+def intersect(m_high: np.ndarray, m_low: np.ndarray) -> np.ndarray:
+    """Merge variant (Prism review, weaknesses paragraph: the union may
+    over-select): a block is kept only when both branches keep it."""
+    return (m_high.astype(bool) & m_low.astype(bool)).astype(np.uint8)
+
+
+def mix_mask(S_high: np.ndarray, S_low: np.ndarray, p: float, causal: bool) -> np.ndarray:
+    """Weighted-merge variant (same paragraph): one Top-P, at the same p, on
+    the equal-weight mixture of the two branches' block distributions."""
+    return top_p_mask(0.5 * (S_high + S_low), p, causal)
+
+
+def merge_masks(r: dict, p: float, causal: bool, merge: str = "union") -> np.ndarray:
+    """The final block mask of one head from its branch results r."""
+    if merge == "union":
+        return union(r["m_high"], r["m_low"])
+    if merge == "intersect":
+        return intersect(r["m_high"], r["m_low"])
+    if merge == "mix":
+        return mix_mask(r["S_high"], r["S_low"], p, causal)
+    raise ValueError(merge)
+
+
+# ------------------------------------------- per-head adaptive band split
+def pair_energy(xbar: np.ndarray, rope_layout: str = "interleaved") -> np.ndarray:
+    """Pooled energy of each RoPE pair, averaged over the blocks: [d/2], the
+    fastest pair first (pair j = dims 2j, 2j+1 interleaved, j and j + d/2
+    rotate-half)."""
+    d = xbar.shape[1]
+    if rope_layout == "interleaved":
+        a, b = xbar[:, 0::2], xbar[:, 1::2]
+    else:
+        a, b = xbar[:, : d // 2], xbar[:, d // 2:]
+    return np.mean(a ** 2 + b ** 2, axis=0)
+
+
+SPLIT_STEP = 8          # pairs: adaptive band edges move in steps of 16 dims
+SPLIT_SHARE_RTOL = 1e-9  # an energy share equal to the reference within rounding counts as reaching it
+
+
+def adaptive_split(spectra: np.ndarray, d: int, d_high: int, d_low: int) -> list[tuple[int, int]]:
+    """Per-head (d_high, d_low) from the heads' pair spectra [H, d/2]
+    (P_j = pooled energy of pair j of Qbar times that of Kbar).
+
+    The reference share is the fraction of the mean spectrum (over the H
+    heads) that the static high band's d_high/2 pairs hold. Head h's high
+    band is [0, j_h) with j_h the smallest multiple of SPLIT_STEP pairs whose
+    cumulative share of the head's own spectrum reaches the reference (within
+    SPLIT_SHARE_RTOL), limited so both bands keep at least SPLIT_STEP pairs;
+    its low band is [j_h - o, d/2) with o = (d_high + d_low - d) / 2 the
+    static overlap in pairs (negative: a gap). A head whose spectrum is zero
+    keeps the static split. Needs d_high, d_low multiples of 2 * SPLIT_STEP.
+    """
+    npairs = d // 2
+    if d_high % (2 * SPLIT_STEP) or d_low % (2 * SPLIT_STEP):
+        raise ValueError("adaptive split needs band widths in multiples of 16 dims")
+    o = (d_high + d_low - d) // 2
+    j0 = d_high // 2
+    mean = spectra.mean(axis=0)
+    cm = np.cumsum(mean)
+    share = cm[j0 - 1] / cm[-1] if cm[-1] > 0 else 0.0
+    lo_j = max(SPLIT_STEP, o)
+    hi_j = min(npairs - SPLIT_STEP, npairs + o - SPLIT_STEP)
+    out = []
+    for P in spectra:
+        c = np.cumsum(P)
+        if c[-1] <= 0 or cm[-1] <= 0:
+            out.append((d_high, d_low))
+            continue
+        jh = hi_j
+        for j in range(lo_j, hi_j + 1, SPLIT_STEP):
+            if c[j - 1] / c[-1] >= share * (1.0 - SPLIT_SHARE_RTOL):
+                jh = j
+                break
+        out.append((2 * jh, d - 2 * (jh - o)))
+    return out
+
+
 # ------------------------------------------------------- grouped-query heads
 def kv_head(h: int, hq: int, hkv: int) -> int:
     """KV head read by query head h under grouped-query attention: the Hq query
@@ -229,11 +322,13 @@ def kv_head(h: int, hq: int, hkv: int) -> int:
 # ------------------------------------------------------- steps (1)-(7) together
 def estimate_head(qh: np.ndarray, kg: np.ndarray, *, block: int, d_high: int, d_low: int, p: float,
                   causal: bool = True, rope_layout: str = "interleaved", tau_mode: str = "fullspec",
-                  kbar: np.ndarray | None = None) -> dict:
-    """The estimator for one query head: qh [N, d], kg [N, d] (its KV head)."""
-    d = qh.shape[1]
+                  kbar: np.ndarray | None = None, merge: str = "union", qbar: np.ndarray | None = None) -> dict:
+    """The estimator for one query head: qh [N, d], kg [N, d] (its KV head);
+    qbar / kbar may be passed already pooled."""
+    d = (qh if qh is not None else qbar).shape[1]
     hi, lo, full = band_dims(d, d_high, d_low, rope_layout)
-    qbar = mean_pool(qh, block)
+    if qbar is None:
+        qbar = mean_pool(qh, block)
     if kbar is None:
         kbar = mean_pool(kg, block)
     tau_h, deg_h = temperature(qbar, kbar, hi, full, tau_mode)
@@ -246,24 +341,29 @@ def estimate_head(qh: np.ndarray, kg: np.ndarray, *, block: int, d_high: int, d_
     L_l, S_l = band_scores(qbar, kbar, lo, tau_l, causal, *fl)
     m_h = top_p_mask(S_h, p, causal)
     m_l = top_p_mask(S_l, p, causal)
+    r = {"m_high": m_h, "m_low": m_l, "S_high": S_h, "S_low": S_l}
     return {
         "qbar": qbar, "kbar": kbar,
         "rms_q": (band_rms(qbar, hi), band_rms(qbar, lo), band_rms(qbar, full)),
         "rms_k": (band_rms(kbar, hi), band_rms(kbar, lo), band_rms(kbar, full)),
         "tau": (tau_h, tau_l), "degenerate": int(deg_h) + int(deg_l),
         "L_high": L_h, "L_low": L_l, "S_high": S_h, "S_low": S_l,
-        "m_high": m_h, "m_low": m_l, "mask": union(m_h, m_l),
+        "m_high": m_h, "m_low": m_l, "mask": merge_masks(r, p, causal, merge),
+        "bands": (d_high, d_low),
     }
 
 
 def estimate(q: np.ndarray, k: np.ndarray, *, block: int, d_high: int, d_low: int, p: float,
              causal: bool = True, rope_layout: str = "interleaved", tau_mode: str = "fullspec",
-             heads=None, keep=False) -> dict:
+             heads=None, keep=False, merge: str = "union", band_mode: str = "static") -> dict:
     """Estimator over q [b, N, Hq, d], k [b, N, Hkv, d] (float64, BSHD).
 
-    Query head h reads KV head h // (Hq/Hkv) (grouped-query attention).
-    Returns mask [b, Hq, nb, nb] (uint8), tau [b, Hq, 2], and, with keep=True,
-    the per-head intermediate dicts.
+    Query head h reads KV head kv_head(h, Hq, Hkv) (grouped-query attention).
+    band_mode 'adaptive' chooses each head's bands with adaptive_split from
+    the spectra of all Hq query heads of the batch entry (whatever `heads`
+    selects for the output). Returns mask [b, Hq, nb, nb] (uint8), tau
+    [b, Hq, 2], bands [b, Hq, 2] (d_high, d_low per head) and, with
+    keep=True, the per-head intermediate dicts.
     """
     b, N, Hq, d = q.shape
     Hkv = k.shape[2]
@@ -273,21 +373,31 @@ def estimate(q: np.ndarray, k: np.ndarray, *, block: int, d_high: int, d_low: in
     heads = range(Hq) if heads is None else heads
     mask = np.zeros((b, Hq, nb, nb), dtype=np.uint8)
     tau = np.zeros((b, Hq, 2))
+    bands = np.zeros((b, Hq, 2), dtype=np.int64)
     per = {}
-    kbars = {}
     for bb in range(b):
+        kbars = {g: mean_pool(k[bb, :, g, :], block) for g in range(Hkv)}
+        qbars = {}
+        split = None
+        if band_mode == "adaptive":
+            qbars = {h: mean_pool(q[bb, :, h, :], block) for h in range(Hq)}
+            ek = {g: pair_energy(kbars[g], rope_layout) for g in kbars}
+            spectra = np.stack([pair_energy(qbars[h], rope_layout) * ek[kv_head(h, Hq, Hkv)] for h in range(Hq)])
+            split = adaptive_split(spectra, d, d_high, d_low)
+        elif band_mode != "static":
+            raise ValueError(band_mode)
         for h in heads:
             g = kv_head(h, Hq, Hkv)
-            if (bb, g) not in kbars:
-                kbars[(bb, g)] = mean_pool(k[bb, :, g, :], block)
-            r = estimate_head(q[bb, :, h, :], k[bb, :, g, :], block=block, d_high=d_high, d_low=d_low,
-                              p=p, causal=causal, rope_layout=rope_layout, tau_mode=tau_mode,
-                              kbar=kbars[(bb, g)])
+            dh, dl = split[h] if split is not None else (d_high, d_low)
+            r = estimate_head(q[bb, :, h, :] if h not in qbars else None, None, block=block, d_high=dh, d_low=dl,
+                              p=p, causal=causal, rope_layout=rope_layout, tau_mode=tau_mode, kbar=kbars[g],
+                              merge=merge, qbar=qbars.get(h))
             mask[bb, h] = r["mask"]
             tau[bb, h] = r["tau"]
+            bands[bb, h] = (dh, dl)
             if keep:
                 per[(bb, h)] = r
-    return {"mask": mask, "tau": tau, "per_head": per}
+    return {"mask": mask, "tau": tau, "bands": bands, "per_head": per}
 
 
 # ------------------------------------------------------ block-sparse attention

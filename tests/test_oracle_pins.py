@@ -451,6 +451,144 @@ def test_gqa_mapping_attention_matches_torch_gqa():
     assert gqa_attention_error(Hq=8, Hkv=4) < 1e-12
 
 
+# ------------------------------------------- merge variants (weaknesses paragraph)
+def merge_case(merge, d_high=64, d_low=96, p=0.9, seed=31):
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=2600, hq=2, hkv=1, seed=seed)
+    from synth import make_qkv, to_f64
+    q, k, _ = make_qkv(w, with_v=False)
+    return po.estimate(to_f64(q, "bf16"), to_f64(k, "bf16"), block=128, d_high=d_high, d_low=d_low, p=p,
+                       merge=merge, keep=True)
+
+
+def intersect_error():
+    """intersection = blocks both branches keep: a subset of each branch and
+    of the union, and equal to them when the bands coincide"""
+    r = merge_case("intersect")
+    bad = 0
+    for key, rr in r["per_head"].items():
+        m = rr["mask"].astype(bool)
+        bad += int((m & ~rr["m_high"].astype(bool)).sum() + (m & ~rr["m_low"].astype(bool)).sum())
+        bad += int((rr["m_high"].astype(bool) & rr["m_low"].astype(bool) & ~m).sum())
+    same = merge_case("intersect", d_high=128, d_low=128)
+    for rr in same["per_head"].values():
+        bad += int((rr["mask"] != rr["m_high"]).sum())
+    return bad
+
+
+def mix_bruteforce_error(trials=200, seed=5):
+    """weighted merge on random tiny rows: the kept set is the minimum-size
+    subset of the mixture (S_high + S_low) / 2 whose mass reaches p (found
+    by enumeration); the kept mass reaches p"""
+    rng = np.random.default_rng(seed)
+    bad = 0
+    for _ in range(trials):
+        n = int(rng.integers(1, 10))
+        sh, sl = rng.dirichlet(np.ones(n) * 0.7), rng.dirichlet(np.ones(n) * 0.7)
+        p = float(rng.uniform(0.3, 0.99))
+        # square non-causal score matrices (every row the same distribution); row 0 is checked
+        sel = po.mix_mask(np.tile(sh, (n, 1)), np.tile(sl, (n, 1)), p, causal=False)[0].astype(bool)
+        mixv = 0.5 * (sh + sl)
+        best = None
+        for size in range(1, n + 1):
+            for sub in itertools.combinations(range(n), size):
+                if mixv[list(sub)].sum() >= p:
+                    best = size
+                    break
+            if best:
+                break
+        bad += int(sel.sum() != best) + int(mixv[sel].sum() < p - 1e-12)
+    return bad
+
+
+def test_intersect_semantics():
+    assert intersect_error() == 0
+
+
+def test_mix_is_top_p_of_the_equal_weight_mixture():
+    assert mix_bruteforce_error() == 0
+    # identical branches: the mixture is the branch itself
+    same = merge_case("mix", d_high=128, d_low=128)
+    for rr in same["per_head"].values():
+        assert np.array_equal(rr["mask"], rr["m_high"])
+
+
+# ------------------------------------------- per-head adaptive band split
+def spectral_heads(profiles, layout="interleaved", base=5e5, B=128, nb=6):
+    """Query heads whose pre-rotation vector is one constant x_h per head
+    (|x_h pair j|^2 = profiles[h][j]) and one KV head with x = 1 in every
+    pair, over nb full blocks; returns q, k [1, N, H, d] post-RoPE."""
+    d = 128
+    N = nb * B
+    cos, sin = rope_tables(N, d, base)
+    H = len(profiles)
+    q = np.zeros((1, N, H, d))
+    for h, prof in enumerate(profiles):
+        x = np.zeros(d)
+        amp = np.sqrt(np.asarray(prof, float))
+        if layout == "interleaved":
+            x[0::2] = amp
+        else:
+            x[: d // 2] = amp
+        q[0, :, h, :] = apply_rope(np.tile(x, (N, 1)), cos, sin, layout)
+    xk = np.zeros(d)
+    if layout == "interleaved":
+        xk[0::2] = 1.0
+    else:
+        xk[: d // 2] = 1.0
+    k = apply_rope(np.tile(xk, (N, 1)), cos, sin, layout)[None, :, None, :]
+    return q, k
+
+
+def closed_form_split(profiles, base=5e5, B=128, d_high=64, d_low=96):
+    """The split rule evaluated on the closed-form pooled spectra: pair j of a
+    constant vector pooled over a full block keeps D_B(theta_j)^2 of its
+    energy (Dirichlet kernel), so P_j = D^2 |x_j|^2 * D^2 * 1."""
+    th = freqs(128, base)
+    D2 = dirichlet(B, th) ** 2
+    spectra = np.stack([D2 * np.asarray(prof, float) * D2 for prof in profiles])
+    mean = spectra.mean(axis=0)
+    share = mean[: d_high // 2].sum() / mean.sum()
+    o = (d_high + d_low - 128) // 2
+    out = []
+    for P in spectra:
+        c = np.cumsum(P) / P.sum()
+        jh = next(j for j in range(max(8, o), 64 - 8 + 1, 8) if c[j - 1] >= share * (1 - 1e-9))
+        out.append((2 * jh, 128 - 2 * (jh - o)))
+    return out
+
+
+def adaptive_split_error(layout="interleaved"):
+    """oracle splits vs the closed form on heads whose energy sits in slow,
+    fast, transition and all pairs (the cases differ by at least 8 pairs)"""
+    j = np.arange(64)
+    profiles = [np.ones(64), (j >= 40).astype(float), ((j >= 12) & (j < 36)).astype(float) + 0.01,
+                np.exp(-j / 10.0)]
+    q, k = spectral_heads(profiles, layout)
+    r = po.estimate(q, k, block=128, d_high=64, d_low=96, p=0.9, band_mode="adaptive", rope_layout=layout)
+    got = [tuple(x) for x in r["bands"][0].tolist()]
+    want = closed_form_split(profiles)
+    return got, want
+
+
+@pytest.mark.parametrize("layout", ["interleaved", "half"])
+def test_adaptive_split_closed_form(layout):
+    got, want = adaptive_split_error(layout)
+    assert got == want
+    assert len(set(want)) >= 3  # the heads really get different splits
+    assert all(dh + dl == 160 for dh, dl in want)
+
+
+def test_adaptive_split_identical_heads_keep_static():
+    """every head with the same spectrum (here the same input) gets the static
+    split back, whatever the spectrum; scaling all queries changes nothing"""
+    j = np.arange(64)
+    for prof in (np.ones(64), np.exp(-j / 7.0), (j % 3 == 0).astype(float) + 0.1):
+        q, k = spectral_heads([prof, prof, prof])
+        for scale in (1.0, 37.0):
+            r = po.estimate(q * scale, k, block=128, d_high=64, d_low=96, p=0.9, band_mode="adaptive")
+            assert r["bands"][0].tolist() == [[64, 96]] * 3
+
+
 # --------------------------------------------- planted mistakes must be caught
 def test_planted_swapped_bands_caught(monkeypatch):
     good = po.band_dims
@@ -537,3 +675,22 @@ def test_planted_interleaved_gqa_mapping_caught(monkeypatch):
     monkeypatch.setattr(po, "kv_head", lambda h, hq, hkv: h % hkv)
     assert gqa_estimate_error() > 0
     assert gqa_attention_error() > 1e-3
+
+
+def test_planted_union_for_intersection_caught(monkeypatch):
+    monkeypatch.setattr(po, "intersect", po.union)
+    assert intersect_error() > 0
+
+
+def test_planted_mix_without_halving_caught(monkeypatch):
+    # the mixture's two distributions added without the 1/2 weights: mass 2, p then reached too early
+    monkeypatch.setattr(po, "mix_mask", lambda sh, sl, p, causal: po.top_p_mask(sh + sl, p, causal))
+    assert mix_bruteforce_error() > 0
+
+
+def test_planted_split_from_the_slow_end_caught(monkeypatch):
+    # spectra read slowest pair first
+    orig = po.pair_energy
+    monkeypatch.setattr(po, "pair_energy", lambda xbar, layout="interleaved": orig(xbar, layout)[::-1])
+    got, want = adaptive_split_error()
+    assert got != want
