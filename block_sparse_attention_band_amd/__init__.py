@@ -24,6 +24,8 @@ __all__ = ["EstimatorConfig", "estimate", "estimate_noalloc", "block_sparse_attn
 _ROPE = {"interleaved": _abi.ROPE_INTERLEAVED, "half": _abi.ROPE_HALF}
 _TAU = {"fullspec": _abi.TAU_FULLSPEC, "none": _abi.TAU_NONE, "unit": _abi.TAU_UNIT,
         "pervec": _abi.TAU_PERVEC}
+_MERGE = {"union": _abi.MERGE_UNION, "intersect": _abi.MERGE_INTERSECT, "mix": _abi.MERGE_MIX}
+_BANDS = {"static": _abi.BANDS_STATIC, "adaptive": _abi.BANDS_ADAPTIVE}
 
 
 @dataclass(frozen=True)
@@ -38,6 +40,8 @@ class EstimatorConfig:
     rope_layout: str = "interleaved"
     tau_mode: str = "fullspec"
     keep_logits: bool = False  # also store the band logits in the workspace (inspection)
+    merge: str = "union"       # "union" (the pages' step 7), "intersect" or "mix"
+    band_mode: str = "static"  # "static" (the pages' split) or "adaptive" (per head)
 
 
 def _torch():
@@ -83,7 +87,8 @@ def _cfg(cfg: EstimatorConfig, workspace=None) -> PrismCfg:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return PrismCfg(cfg.block_size, cfg.d_high, cfg.d_low, cfg.p, int(bool(cfg.causal)), _ROPE[cfg.rope_layout],
-                    _TAU[cfg.tau_mode], _abi.EST_KEEP_LOGITS if cfg.keep_logits else 0, ws_ptr, ws_bytes)
+                    _TAU[cfg.tau_mode], _abi.EST_KEEP_LOGITS if cfg.keep_logits else 0, _MERGE[cfg.merge],
+                    _BANDS[cfg.band_mode], ws_ptr, ws_bytes)
 
 
 def _stream(t) -> int:

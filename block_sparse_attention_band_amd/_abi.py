@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 5
+PRISM_ABI_VERSION = 6
 
 # prism_status_t
 (OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH,
@@ -25,6 +25,8 @@ BF16, FP32 = 0, 1
 ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 TAU_FULLSPEC, TAU_NONE, TAU_UNIT, TAU_PERVEC = 0, 1, 2, 3
 MASK_U8, MASK_BITS = 0, 1
+MERGE_UNION, MERGE_INTERSECT, MERGE_MIX = 0, 1, 2
+BANDS_STATIC, BANDS_ADAPTIVE = 0, 1
 EST_KEEP_LOGITS = 1
 
 
@@ -49,7 +51,8 @@ class PrismCfg(ctypes.Structure):
     _fields_ = [
         ("block_size", ctypes.c_int32), ("d_high", ctypes.c_int32), ("d_low", ctypes.c_int32), ("p", ctypes.c_float),
         ("causal", ctypes.c_int32), ("rope_layout", ctypes.c_int32), ("tau_mode", ctypes.c_int32),
-        ("flags", ctypes.c_int32), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("flags", ctypes.c_int32), ("merge", ctypes.c_int32), ("band_mode", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -57,7 +60,8 @@ class PrismWorkspaceLayout(ctypes.Structure):
     _fields_ = [
         ("qbar_offset", ctypes.c_size_t), ("kbar_offset", ctypes.c_size_t), ("qsq_offset", ctypes.c_size_t),
         ("ksq_offset", ctypes.c_size_t), ("tau_offset", ctypes.c_size_t), ("logits_offset", ctypes.c_size_t),
-        ("logits_plane", ctypes.c_int64), ("total_bytes", ctypes.c_size_t),
+        ("logits_plane", ctypes.c_int64), ("spectrum_offset", ctypes.c_size_t), ("split_offset", ctypes.c_size_t),
+        ("total_bytes", ctypes.c_size_t),
         ("nb", ctypes.c_int64), ("seg_lo", ctypes.c_int32), ("seg_hi", ctypes.c_int32),
         ("overlap", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]

@@ -261,7 +261,135 @@ __global__ __launch_bounds__(kThreads) void tau_kernel(TauArgs a) {
   }
 }
 
+// Adaptive bands, step 1: the pooled spectrum of one head of one tensor, the
+// mean over blocks of each RoPE pair's energy (canonical dims 2j, 2j + 1), in
+// fp64 with a fixed summation order (deterministic). Thread t sums pair
+// t % 64 over blocks t / 64, t / 64 + 4, ...; the four partial sums are added
+// in order.
+__global__ __launch_bounds__(kThreads) void spectrum_kernel(SpectrumArgs a) {
+  __shared__ double red[kThreads / 64][64];
+  const int hh = blockIdx.x, b = blockIdx.y;
+  const int t = hh < a.hq ? 0 : 1;
+  const int H = t ? a.hkv : a.hq;
+  const int h = t ? hh - a.hq : hh;
+  const float *x = a.xbar[t] + ((int64_t)b * H + h) * a.nb * kHeadDim;
+  const int pr = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  double acc = 0.0;
+  for (int i = grp; i < a.nb; i += kThreads / 64) {
+    const float2 v = *reinterpret_cast<const float2 *>(x + (int64_t)i * kHeadDim + 2 * pr);
+    acc += (double)v.x * v.x + (double)v.y * v.y;
+  }
+  red[grp][pr] = acc;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    double sum = 0.0;
+#pragma unroll
+    for (int g = 0; g < kThreads / 64; ++g) sum += red[g][pr];
+    a.spec[((int64_t)b * (a.hq + a.hkv) + hh) * 64 + pr] = sum / a.nb;
+  }
+}
+
+// Adaptive bands, step 2 (one workgroup per batch entry): P_j(h) = spectrum of
+// query head h times that of its KV head; the reference share is the share of
+// the static high band's d_high / 2 pairs in the mean of P over the query
+// heads; head h's high band is [0, j_h) with j_h the smallest multiple of 8
+// pairs whose cumulative share of P(h) reaches the reference (relative
+// tolerance 1e-9), each band keeping at least 8 pairs, and its low band
+// [j_h - o, 64) with o = (d_high + d_low - 128) / 2. Sums run in pair order
+// in fp64. Then each head's temperatures from its bands' energies, as the
+// tau kernel computes them (the energies of a band are the sum of its pairs').
+__global__ __launch_bounds__(kThreads) void split_kernel(SplitArgs a) {
+  __shared__ double mean_s[64];
+  __shared__ double ref_share;
+  const int b = blockIdx.x;
+  const int G = a.hq / a.hkv;
+  const double *sq = a.spec + (int64_t)b * (a.hq + a.hkv) * 64;
+  const double *sk = sq + (int64_t)a.hq * 64;
+  if (threadIdx.x < 64) {
+    const int j = threadIdx.x;
+    double m = 0.0;
+    for (int h = 0; h < a.hq; ++h) m += sq[h * 64 + j] * sk[(h / G) * 64 + j];
+    mean_s[j] = m / a.hq;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double c = 0.0, cj0 = 0.0;
+    for (int j = 0; j < 64; ++j) {
+      c += mean_s[j];
+      if (j == a.d_high / 2 - 1) cj0 = c;
+    }
+    ref_share = c > 0.0 ? cj0 / c : -1.0;
+  }
+  __syncthreads();
+  const int o = (a.d_high + a.d_low - kHeadDim) / 2;
+  const int lo_j = max(8, o), hi_j = min(56, 64 + o - 8);
+  for (int h = threadIdx.x; h < a.hq; h += blockDim.x) {
+    const double *pq = sq + h * 64, *pk = sk + (h / G) * 64;
+    double tot = 0.0;
+    for (int j = 0; j < 64; ++j) tot += pq[j] * pk[j];
+    int jh = a.d_high / 2;
+    if (tot > 0.0 && ref_share >= 0.0) {
+      jh = hi_j;
+      double c = 0.0;
+      for (int j = 0; j < 64; ++j) {
+        c += pq[j] * pk[j];
+        if ((j + 1) % 8 == 0 && j + 1 >= lo_j && j + 1 <= hi_j && c / tot >= ref_share * (1.0 - 1e-9)) {
+          jh = j + 1;
+          break;
+        }
+      }
+    }
+    const int dh = 2 * jh, dl = kHeadDim - 2 * (jh - o), lstart = 2 * (jh - o);
+    int32_t *sp = a.split + ((int64_t)b * a.hq + h) * 4;
+    sp[0] = min(dh, lstart);
+    sp[1] = max(dh, lstart);
+    sp[2] = dh;
+    sp[3] = dl;
+    // band energies (sums of pair energies) and RMS
+    double e[2][3] = {{0.0, 0.0, 0.0}, {0.0, 0.0, 0.0}};
+    for (int j = 0; j < 64; ++j) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const double v = t ? pk[j] : pq[j];
+        if (j < jh) e[t][0] += v;
+        if (j >= jh - o) e[t][1] += v;
+        e[t][2] += v;
+      }
+    }
+    double r[6];
+    for (int t = 0; t < 2; ++t) {
+      r[3 * t + 0] = sqrt(e[t][0] / dh);
+      r[3 * t + 1] = sqrt(e[t][1] / dl);
+      r[3 * t + 2] = sqrt(e[t][2] / kHeadDim);
+    }
+    double th = 1.0, tl = 1.0;
+    const bool okh = r[0] > 0 && r[3] > 0 && r[2] > 0 && r[5] > 0;
+    const bool okl = r[1] > 0 && r[4] > 0 && r[2] > 0 && r[5] > 0;
+    if (a.tau_mode == 0) {
+      if (okh) th = (r[0] * r[3]) / (r[2] * r[5]);
+      if (okl) tl = (r[1] * r[4]) / (r[2] * r[5]);
+    } else if (a.tau_mode == 2) {
+      if (okh) th = r[0] * r[3];
+      if (okl) tl = r[1] * r[4];
+    }
+    float *out = a.tau + ((int64_t)b * a.hq + h) * 8;
+    out[0] = (float)th; out[1] = (float)tl;
+    out[2] = (float)r[0]; out[3] = (float)r[1]; out[4] = (float)r[2];
+    out[5] = (float)r[3]; out[6] = (float)r[4]; out[7] = (float)r[5];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_spectrum(const SpectrumArgs &a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(spectrum_kernel, dim3(a.hq + a.hkv, batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const SplitArgs &a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(split_kernel, dim3(batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s) {
   int dev = 0, cus = 0;

@@ -86,8 +86,16 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (cfg->rope_layout != PRISM_ROPE_INTERLEAVED && cfg->rope_layout != PRISM_ROPE_HALF) return PRISM_ERR_CONFIG;
   if (cfg->tau_mode < PRISM_TAU_FULLSPEC || cfg->tau_mode > PRISM_TAU_PERVEC) return PRISM_ERR_CONFIG;
   if (cfg->flags & ~PRISM_EST_KEEP_LOGITS) return PRISM_ERR_CONFIG;
+  if (cfg->merge < PRISM_MERGE_UNION || cfg->merge > PRISM_MERGE_MIX) return PRISM_ERR_CONFIG;
+  if (cfg->band_mode != PRISM_BANDS_STATIC && cfg->band_mode != PRISM_BANDS_ADAPTIVE) return PRISM_ERR_CONFIG;
+  if (cfg->band_mode == PRISM_BANDS_ADAPTIVE &&
+      (cfg->d_high % 16 || cfg->d_low % 16 || cfg->tau_mode == PRISM_TAU_PERVEC))
+    return PRISM_ERR_CONFIG;
   if (cfg->block_size != kBlock) return PRISM_ERR_UNSUPPORTED;
   if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
+  // the mixture merge selects both branches' rows in one wave: fused path only
+  if (cfg->merge == PRISM_MERGE_MIX && (seq + kBlock - 1) / kBlock > prism::kFusedMaxBlocks)
+    return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
 }
 
@@ -112,6 +120,9 @@ void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_c
   const bool logits = nb > prism::kFusedMaxBlocks || (cfg->flags & PRISM_EST_KEEP_LOGITS);
   L->logits_plane = logits ? prism::logit_plane(nb, cfg->causal) : 0;
   L->logits_offset = off; off = round_up(off + b * q->heads * 2 * (size_t)L->logits_plane * 4, 256);
+  const bool adaptive = cfg->band_mode == PRISM_BANDS_ADAPTIVE;
+  L->spectrum_offset = off; off = round_up(off + (adaptive ? b * (q->heads + k->heads) * (kHeadDim / 2) * 8 : 0), 256);
+  L->split_offset = off;    off = round_up(off + (adaptive ? b * q->heads * 16 : 0), 256);
   L->total_bytes = off;
   L->nb = nb;
   const int lo_start = kHeadDim - cfg->d_low;
@@ -245,6 +256,8 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   sc.ksq = pa.sq[1];
   sc.pervec = cfg->tau_mode == PRISM_TAU_PERVEC;
   sc.keep_logits = L.logits_plane > 0;
+  const bool adaptive = cfg->band_mode == PRISM_BANDS_ADAPTIVE;
+  sc.split = adaptive ? reinterpret_cast<const int32_t *>(ws + L.split_offset) : nullptr;
 
   prism::TopPArgs tp;
   tp.logits = sc.logits;
@@ -257,6 +270,7 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   tp.batch = (int)q->batch;
   tp.causal = cfg->causal;
   tp.p = cfg->p;
+  tp.merge = cfg->merge;
 
   const int per_chunk_max = fp32 ? 8 : 16;  // heads one 256-thread workgroup covers per token
   const int nh[2] = {ta.hq, ta.hkv};
@@ -270,7 +284,28 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   ta.h0 = 0;
   ta.nh = ta.hq;
   if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
-  if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  if (adaptive) {
+    prism::SpectrumArgs sa;
+    sa.xbar[0] = pa.xbar[0];
+    sa.xbar[1] = pa.xbar[1];
+    sa.spec = reinterpret_cast<double *>(ws + L.spectrum_offset);
+    sa.hq = ta.hq;
+    sa.hkv = ta.hkv;
+    sa.nb = nb;
+    prism::SplitArgs sp;
+    sp.spec = sa.spec;
+    sp.tau = ta.tau;
+    sp.split = reinterpret_cast<int32_t *>(ws + L.split_offset);
+    sp.hq = ta.hq;
+    sp.hkv = ta.hkv;
+    sp.d_high = cfg->d_high;
+    sp.d_low = cfg->d_low;
+    sp.tau_mode = cfg->tau_mode;
+    if (prism::launch_spectrum(sa, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+    if (prism::launch_split(sp, (int)q->batch, s) != hipSuccess) return PRISM_ERR_LAUNCH;
+  } else if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) {
+    return PRISM_ERR_LAUNCH;
+  }
   sc.h0 = tp.h0 = 0;
   sc.nh = tp.nh = ta.hq;
   if (nb <= prism::kFusedMaxBlocks) {

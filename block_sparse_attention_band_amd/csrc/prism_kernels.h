@@ -36,6 +36,22 @@ struct PoolArgs {
   int32_t seg_lo, seg_hi;
 };
 
+// Adaptive bands: per-pair pooled spectra, then each head's split and
+// temperatures from them.
+struct SpectrumArgs {
+  const float *xbar[2];    // Qbar [batch][Hq][nb][128], Kbar [batch][Hkv][nb][128] (canonical order)
+  double *spec;            // [batch][Hq + Hkv][64]: mean over blocks of each pair's energy
+  int32_t hq, hkv, nb;
+};
+struct SplitArgs {
+  const double *spec;      // as written by the spectrum kernel
+  float *tau;              // [batch][Hq][8], as the tau kernel's
+  int32_t *split;          // [batch][Hq][4]: seg_lo, seg_hi, d_high, d_low
+  int32_t hq, hkv;
+  int32_t d_high, d_low;   // the static split the rule starts from
+  int32_t tau_mode;        // FULLSPEC, NONE or UNIT
+};
+
 struct TauArgs {
   const float *qsq, *ksq;  // [batch][H][nb][4]
   float *tau;              // [batch][Hq][8]
@@ -70,6 +86,7 @@ struct ScoreArgs {
   const float *qsq, *ksq;  // per-block segment energies (per-vector temperature)
   int32_t pervec;          // 1: scale logits by the per-vector band factors
   int32_t keep_logits;     // fused kernel: also store the logits in the planes
+  const int32_t *split;    // adaptive bands: [batch][Hq][4] per head (seg_lo, seg_hi, d_high, d_low); else null
 };
 
 struct TopPArgs {
@@ -82,10 +99,13 @@ struct TopPArgs {
   int32_t h0, nh;          // query heads h0 .. h0 + nh - 1
   int32_t causal;
   float p;
+  int32_t merge;           // prism_merge_t
 };
 
 hipError_t launch_pool(const PoolArgs &a, int batch, int fp32, hipStream_t s);
 hipError_t launch_tau(const TauArgs &a, int batch, hipStream_t s);
+hipError_t launch_spectrum(const SpectrumArgs &a, int batch, hipStream_t s);
+hipError_t launch_split(const SplitArgs &a, int batch, hipStream_t s);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s);
 // both at once, logits kept on chip (nb <= kFusedMaxBlocks)

@@ -325,6 +325,53 @@ __device__ __forceinline__ uint32_t select_row_radix(const float (&x)[EPL], int 
   return sel[0];
 }
 
+// Weighted merge (prism_merge_t MIX): one Top-P on the equal-weight mixture
+// of the two branches' block distributions, v_j = e_high,j / Z_high +
+// e_low,j / Z_low (the weights 1/2 cancel), selected by the same radix rule
+// on log2 v. fp32 throughout; slots past the row hold -inf.
+template <int EPL>
+__device__ uint32_t select_row_mix(const float (&xh)[EPL], const float (&xl)[EPL], int ne4, float p, int lane,
+                                  unsigned long long *bins) {
+  float mh = -INFINITY, ml = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k)
+    if (k / 4 < ne4) {
+      mh = fmaxf(mh, xh[k]);
+      ml = fmaxf(ml, xl[k]);
+    }
+  mh = wave_max(mh);
+  ml = wave_max(ml);
+  float eh[EPL], el[EPL];
+  float zh = 0.f, zl = 0.f;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    eh[k] = k / 4 < ne4 ? __builtin_amdgcn_exp2f(xh[k] - mh) : 0.f;
+    el[k] = k / 4 < ne4 ? __builtin_amdgcn_exp2f(xl[k] - ml) : 0.f;
+    zh += eh[k];
+    zl += el[k];
+  }
+  const float ih = 1.0f / wave_sum(zh), il = 1.0f / wave_sum(zl);
+  float xm[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    const float v = eh[k] * ih + el[k] * il;
+    xm[k] = v > 0.f ? __builtin_amdgcn_logf(v) : -INFINITY;  // v_log_f32: log2
+  }
+  return select_row_radix<EPL>(xm, ne4, p, lane, bins);
+}
+
+// The bands of one head: those of the launch (static split), or the head's
+// own from the split section (adaptive split).
+__device__ __forceinline__ void head_bands(ScoreArgs &a, int64_t bh) {
+  if (a.split) {
+    const int4 v = *reinterpret_cast<const int4 *>(a.split + bh * 4);
+    a.seg_lo = v.x;
+    a.seg_hi = v.y;
+    a.d_high = v.z;
+    a.d_low = v.w;
+  }
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -434,6 +481,7 @@ __global__ __launch_bounds__(256, 2) void score_kernel(ScoreArgs a) {
     }
   }
 
+  head_bands(a, bh);
   const int b = bh / a.hq, h = bh % a.hq, g = h / (a.hq / a.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -614,10 +662,14 @@ __global__ __launch_bounds__(256) void topp_kernel(TopPArgs a) {
   for (int w = 0; w < W; ++w) sel_s[wave][w][lane] = bits[w];
   __syncthreads();
   if (!live || z != 0) return;
-  // union of the branches -> mask row, zeros included
+  // union (or intersection) of the branches -> mask row, zeros included
 #pragma unroll
   for (int w = 0; w < W; ++w)
-    if (2048 * w < a.nb) write_mask_chunk(a, (int64_t)bh * a.nb + i, 2048 * w, 8, bits[w] | sel_s[wave + 1][w][lane], lane);
+    if (2048 * w < a.nb) {
+      const uint32_t other = sel_s[wave + 1][w][lane];
+      write_mask_chunk(a, (int64_t)bh * a.nb + i, 2048 * w, 8,
+                       a.merge == PRISM_MERGE_INTERSECT ? (bits[w] & other) : (bits[w] | other), lane);
+    }
 }
 
 // ---- scores and Top-P in one kernel (rows of at most 1024 blocks)
@@ -646,7 +698,7 @@ constexpr int kFusedChunk = 256;       // key blocks per score chunk
 constexpr int kFusedPitch = kFusedChunk + 4;
 constexpr int kRuntime16 = 100;
 
-template <int LO16, int HI16, bool PV>
+template <int LO16, int HI16, bool PV, bool MIX>
 __global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   __shared__ __attribute__((aligned(16))) float lt[2][kStrip][kFusedPitch];  // [branch][row][key]
@@ -659,6 +711,7 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   const int rank = blockIdx.x / nbh;
   const int I = a.causal ? nI - 1 - rank : rank;  // longest strips first
   const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+  head_bands(a, bh);
   const int b = bh / a.hq, h = bh % a.hq, gk = h / (a.hq / a.hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -823,8 +876,14 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   for (int r = 0; r < 2; ++r) {
     if (!live[r]) continue;
     const int ne4 = (nc[r] + 255) / 256;
-    const uint32_t bits = select_row_radix<16>(xh[r], ne4, t.p, lane, bins_s[wave]) |
-                          select_row_radix<16>(xl[r], ne4, t.p, lane, bins_s[wave]);
+    uint32_t bits;
+    if constexpr (MIX) {  // the mixture's selection is its own instance (registers)
+      bits = select_row_mix<16>(xh[r], xl[r], ne4, t.p, lane, bins_s[wave]);
+    } else {
+      const uint32_t bh_ = select_row_radix<16>(xh[r], ne4, t.p, lane, bins_s[wave]);
+      const uint32_t bl_ = select_row_radix<16>(xl[r], ne4, t.p, lane, bins_s[wave]);
+      bits = t.merge == PRISM_MERGE_INTERSECT ? (bh_ & bl_) : (bh_ | bl_);
+    }
     write_mask_chunk(t, (int64_t)bh * a.nb + iq[r], 0, 4, bits, lane);
   }
 }
@@ -837,8 +896,10 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   int per_head = 0;
   for (int I = 0; I < nI; ++I) per_head += ((a.causal ? I + 1 : nI) + kScoreTilesPerWg - 1) / kScoreTilesPerWg;
   const dim3 grid(per_head * a.nh * a.batch);  // heads x (full chunks, then remainders)
-  const bool def = a.seg_lo == 32 && a.seg_hi == 64, equal = a.seg_lo == 0 && a.seg_hi == 128;
-  const bool by8 = a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0;
+  // per-head bands (multiples of 16) take the run-time segment variant
+  const bool def = !a.split && a.seg_lo == 32 && a.seg_hi == 64;
+  const bool equal = !a.split && a.seg_lo == 0 && a.seg_hi == 128;
+  const bool by8 = a.split || (a.seg_lo % 8 == 0 && a.seg_hi % 8 == 0);
   if (a.pervec) {
     if (def) hipLaunchKernelGGL((score_kernel<4, 8, true>), grid, dim3(256), 0, s, a);
     else if (by8) hipLaunchKernelGGL((score_kernel<kRuntime8, 0, true>), grid, dim3(256), 0, s, a);
@@ -857,18 +918,27 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
 
 hipError_t launch_score_topp(const ScoreArgs &a, const TopPArgs &t, hipStream_t s) {
   const dim3 grid(((a.nb + kStrip - 1) / kStrip) * a.nh * a.batch), block(kFusedWaves * 64);
-  const bool def = a.seg_lo == 32 && a.seg_hi == 64;
-  const bool by16 = a.seg_lo % 16 == 0 && a.seg_hi % 16 == 0;
-  if (a.pervec) {
-    if (def) hipLaunchKernelGGL((score_topp_kernel<2, 4, true>), grid, block, 0, s, a, t);
-    else if (by16) hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, true>), grid, block, 0, s, a, t);
-    else hipLaunchKernelGGL((score_topp_kernel<-1, -1, true>), grid, block, 0, s, a, t);
+  const bool def = !a.split && a.seg_lo == 32 && a.seg_hi == 64;
+  const bool by16 = a.split || (a.seg_lo % 16 == 0 && a.seg_hi % 16 == 0);
+  if (t.merge == PRISM_MERGE_MIX) {
+    if (a.pervec) {
+      if (by16) hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, true, true>), grid, block, 0, s, a, t);
+      else hipLaunchKernelGGL((score_topp_kernel<-1, -1, true, true>), grid, block, 0, s, a, t);
+    } else if (by16) {
+      hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, false, true>), grid, block, 0, s, a, t);
+    } else {
+      hipLaunchKernelGGL((score_topp_kernel<-1, -1, false, true>), grid, block, 0, s, a, t);
+    }
+  } else if (a.pervec) {
+    if (def) hipLaunchKernelGGL((score_topp_kernel<2, 4, true, false>), grid, block, 0, s, a, t);
+    else if (by16) hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, true, false>), grid, block, 0, s, a, t);
+    else hipLaunchKernelGGL((score_topp_kernel<-1, -1, true, false>), grid, block, 0, s, a, t);
   } else if (def) {
-    hipLaunchKernelGGL((score_topp_kernel<2, 4, false>), grid, block, 0, s, a, t);
+    hipLaunchKernelGGL((score_topp_kernel<2, 4, false, false>), grid, block, 0, s, a, t);
   } else if (by16) {
-    hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, false>), grid, block, 0, s, a, t);
+    hipLaunchKernelGGL((score_topp_kernel<kRuntime16, 0, false, false>), grid, block, 0, s, a, t);
   } else {
-    hipLaunchKernelGGL((score_topp_kernel<-1, -1, false>), grid, block, 0, s, a, t);
+    hipLaunchKernelGGL((score_topp_kernel<-1, -1, false, false>), grid, block, 0, s, a, t);
   }
   return hipGetLastError();
 }

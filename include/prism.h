@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 5
+#define PRISM_ABI_VERSION 6
 
 typedef enum {
   PRISM_OK = 0,
@@ -59,7 +59,8 @@ typedef enum {
   PRISM_ERR_SHAPE = 3,       /* sizes inconsistent with each other or non-positive */
   PRISM_ERR_STRIDE = 4,      /* a stride is non-positive or rows would overlap */
   PRISM_ERR_ALIGN = 5,       /* data pointer or row start not 16-byte aligned */
-  PRISM_ERR_CONFIG = 6,      /* d_high, d_low, p, rope_layout or tau_mode out of range */
+  PRISM_ERR_CONFIG = 6,      /* d_high, d_low, p, rope_layout, tau_mode, merge or band_mode out of
+                                range, or a band mode the other settings exclude */
   PRISM_ERR_WORKSPACE = 7,   /* workspace NULL, not 256-byte aligned, or too small */
   PRISM_ERR_UNSUPPORTED = 8, /* valid but not built: head_dim != 128, block != 128, too many blocks */
   PRISM_ERR_LAUNCH = 9,      /* a kernel launch failed */
@@ -120,6 +121,27 @@ typedef struct {
   int32_t reserved;  /* set to 0 */
 } prism_mask_t;
 
+/* How the two branches' masks become the final mask. The pages' step (7) is
+ * the union; the other two answer the weakness the Prism review lists (the
+ * union may over-select) and exist for comparison.
+ * UNION:     M = M_high OR M_low.
+ * INTERSECT: M = M_high AND M_low.
+ * MIX:       one Top-P at p on the equal-weight mixture (S_high + S_low) / 2 of
+ *            the branches' block distributions (up to 1024 blocks). */
+typedef enum { PRISM_MERGE_UNION = 0, PRISM_MERGE_INTERSECT = 1, PRISM_MERGE_MIX = 2 } prism_merge_t;
+
+/* Band split. STATIC: d_high / d_low for every head (the pages' design).
+ * ADAPTIVE (the review's other listed weakness, a static split for heads of
+ * different spectra): per query head, the high band ends at the smallest
+ * multiple of 8 RoPE pairs whose share of the head's pooled spectrum (per
+ * pair: mean pooled energy of Qbar times that of Kbar, fastest pair first)
+ * reaches the share that the static high band's d_high / 2 pairs hold in the
+ * mean spectrum of all query heads (of that batch entry); the low band keeps
+ * the static overlap d_high + d_low - head_dim, and each band keeps at least
+ * 8 pairs. Heads that share one spectrum get the static split. Needs d_high
+ * and d_low multiples of 16 and a tau_mode other than PERVEC. */
+typedef enum { PRISM_BANDS_STATIC = 0, PRISM_BANDS_ADAPTIVE = 1 } prism_band_mode_t;
+
 /* Estimator flags (prism_cfg_t.flags). KEEP_LOGITS: also store both branches'
  * logits in the workspace (see logits_offset) for inspection. Sequences of at
  * most 1024 blocks otherwise keep them on chip: their scores and selection
@@ -135,6 +157,8 @@ typedef struct {
   int32_t rope_layout;/* prism_rope_layout_t */
   int32_t tau_mode;   /* prism_tau_mode_t */
   int32_t flags;      /* 0, or PRISM_EST_KEEP_LOGITS */
+  int32_t merge;      /* prism_merge_t (PRISM_MERGE_UNION: the pages' step (7)) */
+  int32_t band_mode;  /* prism_band_mode_t (PRISM_BANDS_STATIC: the pages' split) */
   void *workspace;    /* device scratch, 256-byte aligned, >= prism_estimate_workspace_bytes() */
   size_t workspace_bytes;
 } prism_cfg_t;
@@ -145,7 +169,9 @@ typedef struct {
  * pair j (for INTERLEAVED this is the physical order). The three segments
  * [0, seg_lo), [seg_lo, seg_hi), [seg_hi, head_dim) of canonical dims are
  * high-only, middle and low-only; the middle one belongs to both bands when
- * `overlap` is 1 (d_high + d_low > head_dim) and to neither when 0. */
+ * `overlap` is 1 (d_high + d_low > head_dim) and to neither when 0. With
+ * PRISM_BANDS_ADAPTIVE the per-block energies and seg_lo / seg_hi are those of
+ * the static split and each head's own segments are in the split section. */
 typedef struct {
   size_t qbar_offset; /* fp32 [batch][Hq][nb][head_dim]: block means of Q */
   size_t kbar_offset; /* fp32 [batch][Hkv][nb][head_dim]: block means of K */
@@ -162,6 +188,10 @@ typedef struct {
                          i * round_up(nb, 4). */
   int64_t logits_plane; /* floats between consecutive logit planes (a multiple of 64); 0 when
                            the logits are not stored */
+  size_t spectrum_offset; /* PRISM_BANDS_ADAPTIVE: fp64 [batch][Hq + Hkv][head_dim / 2], the mean
+                           pooled energy of each RoPE pair (query heads, then KV heads) */
+  size_t split_offset;  /* PRISM_BANDS_ADAPTIVE: int32 [batch][Hq][4], each head's seg_lo,
+                           seg_hi, d_high, d_low (the bands in canonical dims as above) */
   size_t total_bytes; /* == prism_estimate_workspace_bytes() */
   int64_t nb;         /* blocks per sequence, ceil(seq / block_size) */
   int32_t seg_lo, seg_hi, overlap, reserved;

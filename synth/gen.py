@@ -80,7 +80,7 @@ class Workload:
     head_dim: int
     dtype: str  # "bf16" or "fp32"
     theta: float  # RoPE base
-    kind: str  # "iid" (Q,K,V ~ N(0,1)) or "semantic" (0.7*s + 0.7*z)
+    kind: str  # "iid" (Q,K,V ~ N(0,1)), "semantic" (0.7*s + 0.7*z) or "spectral" (s band-limited per group)
     planted: bool  # slash + vertical structure planted in K
     p: float
     block: int = 128
@@ -117,6 +117,11 @@ WORKLOADS = {
     # 16 frames x 32 x 48 patch tokens followed by text.
     "qwen3_8b_yarn_128k": Workload("qwen3_8b_yarn_128k", 6, 1, 131072, 32, 8, 128, "bf16", 1e6, "semantic", False,
                                    0.93, rope=Rope("yarn", factor=4.0, orig_ctx=32768)),
+    # heads that differ in spectrum (the static band split's weakness): a
+    # Llama-3-8B-shaped layer whose KV groups carry their semantic content in
+    # different RoPE pair bands
+    "llama3_8b_spectral_32k": Workload("llama3_8b_spectral_32k", 9, 1, 32768, 32, 8, 128, "bf16", 5e5, "spectral",
+                                       False, 0.95),
     "qwen3_vl_8b_video_32k": Workload("qwen3_vl_8b_video_32k", 7, 1, 32768, 32, 8, 128, "bf16", 5e6, "semantic", False,
                                       0.93, rope=Rope("mrope", mrope="interleaved", sections=(24, 20, 20),
                                                       grid=(16, 32, 48))),
@@ -222,6 +227,25 @@ def _workers() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+def spectral_window(d: int, g: int, hkv: int, rope_layout: str = "interleaved") -> np.ndarray:
+    """Per-dim gain of KV group g's semantic vector in the 'spectral' recipe:
+    RoPE pair j gets exp(-(j - c_g)^2 / (2 * 8^2)) with the centre c_g spread
+    from pair 8 (fast) to pair 56 (slow) over the groups, scaled so the mean
+    squared gain over the pairs is 1 (the same total energy as the isotropic
+    recipe). Both dims of a pair get the pair's gain, in the pair layout of
+    `rope_layout`."""
+    j = np.arange(d // 2, dtype=np.float64)
+    c = 8.0 + 48.0 * g / (hkv - 1) if hkv > 1 else d / 4.0
+    a = np.exp(-((j - c) ** 2) / (2.0 * 8.0 ** 2))
+    a /= np.sqrt(np.mean(a ** 2))
+    out = np.empty(d)
+    if rope_layout == "interleaved":
+        out[0::2], out[1::2] = a, a
+    else:
+        out[: d // 2], out[d // 2:] = a, a
+    return out
+
+
 def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True):
     """Q [b, N, Hq, d], K [b, N, Hkv, d], V [b, N, Hkv, d] in BSHD order.
 
@@ -231,6 +255,9 @@ def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True)
       semantic: Q_h = RoPE(0.7*s_g(h) + 0.7*z), K_g = RoPE(0.7*s_g + 0.7*z'),
                 s_g ~ N(0,1)^d fixed per KV group g and shared by the group's
                 query heads; V ~ N(0,1).
+      spectral: as semantic, with s_g multiplied by spectral_window(g): each
+                KV group's semantic content sits in its own band of RoPE
+                pairs, from the fastest (group 0) to the slowest.
       planted (on top of semantic, on post-RoPE K of each KV group g):
         slash:    K_g[n] += 0.5 * mean_{h in g} Q_h[n + delta_n],
                   delta_n ~ U{1..4} per key (skipped past the end);
@@ -247,11 +274,14 @@ def make_qkv(w: Workload, rope_layout: str = "interleaved", with_v: bool = True)
     v = np.empty((b, N, Hkv, d), st) if with_v else None
 
     def semantic(bb, g):
-        return _rng(w.seed, T_SEMANTIC, g, bb).standard_normal(d, dtype=np.float32).astype(np.float64)
+        s = _rng(w.seed, T_SEMANTIC, g, bb).standard_normal(d, dtype=np.float32).astype(np.float64)
+        if w.kind == "spectral":
+            return s * spectral_window(d, g, Hkv, rope_layout)
+        return s
 
     def pre(bb, tensor_id, head, g):
         z = _rng(w.seed, tensor_id, head, bb).standard_normal((N, d), dtype=np.float32).astype(np.float64)
-        if w.kind == "semantic":
+        if w.kind in ("semantic", "spectral"):
             return 0.7 * semantic(bb, g)[None, :] + 0.7 * z
         return z
 

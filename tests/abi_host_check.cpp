@@ -17,6 +17,8 @@ namespace prism {
 int g_launches = 0;
 hipError_t launch_pool(const PoolArgs &, int, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_tau(const TauArgs &, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_spectrum(const SpectrumArgs &, int, hipStream_t) { ++g_launches; return hipSuccess; }
+hipError_t launch_split(const SplitArgs &, int, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_score(const ScoreArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_topp(const TopPArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_score_topp(const ScoreArgs &, const TopPArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
@@ -90,6 +92,14 @@ int main() {
   CHECK(est(tensor(131073, 32), tensor(131073, 8), cfg(), mask(131073, 32), 4) == PRISM_OK);
   CHECK(est(tensor(1 << 20, 32), tensor(1 << 20, 8), cfg(), mask(1 << 20, 32, 1, PRISM_MASK_BITS), 4) == PRISM_OK);
   CHECK(est(tensor(1, 1), tensor(1, 1), cfg(), mask(1, 1), 3) == PRISM_OK);
+  {  // adaptive bands: pool, spectrum, split, scores + selection
+    prism_cfg_t c = cfg();
+    c.band_mode = PRISM_BANDS_ADAPTIVE;
+    CHECK(est(tensor(131072, 32), tensor(131072, 8), c, mask(131072, 32), 4) == PRISM_OK);
+    c.merge = PRISM_MERGE_MIX;
+    CHECK(est(tensor(4096, 32), tensor(4096, 8), c, mask(4096, 32), 4) == PRISM_OK);
+    CHECK(est(tensor(131073, 32), tensor(131073, 8), c, mask(131073, 32), 4) == PRISM_ERR_UNSUPPORTED);
+  }
   CHECK(attn(tensor(131072, 32), tensor(131072, 8), tensor(131072, 8), mask(131072, 32), tensor(131072, 32)) == PRISM_OK);
 
   // NULLs everywhere
@@ -146,6 +156,8 @@ int main() {
       c = cfg(); c.tau_mode = x; est(q, k, c, m, 3);
       c = cfg(); c.rope_layout = x; est(q, k, c, m, 3);
       c = cfg(); c.flags = x; est(q, k, c, m, 3);
+      c = cfg(); c.merge = x; est(q, k, c, m, 3);
+      c = cfg(); c.band_mode = x; est(q, k, c, m, x == PRISM_BANDS_ADAPTIVE ? 4 : 3);
       prism_mask_t mm = m; mm.format = x; est(q, k, cfg(), mm, 3);
       mm = m; mm.block_size = x; est(q, k, cfg(), mm, 3);
     }

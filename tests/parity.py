@@ -48,10 +48,16 @@ def to_device(x: np.ndarray, dtype: str, layout: str = "bshd"):
 
 
 def oracle_estimate_heads(q, k, dtype, *, block, d_high, d_low, p, causal, rope_layout="interleaved",
-                          tau_mode="fullspec", heads=None):
-    """Per-head oracle results {(b, h): dict} widening one head at a time."""
+                          tau_mode="fullspec", heads=None, merge="union", band_mode="static"):
+    """Per-head oracle results {(b, h): dict} widening one head at a time
+    (adaptive bands need every query head's spectrum, so they widen all)."""
     b, N, Hq, _ = q.shape
     Hkv = k.shape[2]
+    if band_mode == "adaptive":
+        r = po.estimate(to_f64(q, dtype), to_f64(k, dtype), block=block, d_high=d_high, d_low=d_low, p=p,
+                        causal=causal, rope_layout=rope_layout, tau_mode=tau_mode, heads=heads, keep=True,
+                        merge=merge, band_mode=band_mode)
+        return r["per_head"]
     heads = range(Hq) if heads is None else heads
     out = {}
     kbars = {}
@@ -62,7 +68,7 @@ def oracle_estimate_heads(q, k, dtype, *, block, d_high, d_low, p, causal, rope_
                 kbars[(bb, g)] = po.mean_pool(to_f64(k[bb, :, g, :], dtype), block)
             out[(bb, h)] = po.estimate_head(to_f64(q[bb, :, h, :], dtype), None, block=block, d_high=d_high,
                                             d_low=d_low, p=p, causal=causal, rope_layout=rope_layout,
-                                            tau_mode=tau_mode, kbar=kbars[(bb, g)])
+                                            tau_mode=tau_mode, kbar=kbars[(bb, g)], merge=merge)
     return out
 
 
@@ -95,10 +101,27 @@ def _branch_excuses(S, L, sel_oracle, i, J, p):
     return mass_tie, key_tie, gap
 
 
-def compare_masks(gpu_mask: np.ndarray, oracle: dict, p: float, causal: bool) -> dict:
+def decisions(r: dict, merge: str) -> list:
+    """The Top-P decisions a head's mask is made of: the two branches (union,
+    intersection) or the one on the equal-weight mixture; each as
+    (name, S, L, kept) with L the natural-log scores."""
+    if merge == "mix":
+        S = 0.5 * (r["S_high"] + r["S_low"])
+        with np.errstate(divide="ignore"):
+            L = np.where(S > 0, np.log(np.where(S > 0, S, 1.0)), -np.inf)
+        return [("mix", S, L, r["mask"])]
+    return [("high", r["S_high"], r["L_high"], r["m_high"]), ("low", r["S_low"], r["L_low"], r["m_low"])]
+
+
+def compare_masks(gpu_mask: np.ndarray, oracle: dict, p: float, causal: bool, merge: str = "union") -> dict:
     """Classify every differing block of gpu_mask [b, H, nb, nb] against the
     oracle (rule in the module docstring). Returns counts and, for the key
-    ties, the largest oracle gap (log2 units) and its ratio to the window."""
+    ties, the largest oracle gap (log2 units) and its ratio to the window.
+    Which decisions must be excused follows the merge: a union block the
+    oracle keeps needs an excuse in every branch that keeps it, one it drops
+    in some branch; an intersection block the oracle keeps needs one in some
+    branch, one it drops in every branch that drops it; a mixture block in
+    the one decision."""
     stats = {"blocks": 0, "mismatch": 0, "mass_tie": 0, "score_tie": 0, "unexcused": 0, "where": [],
              "max_key_gap": 0.0, "max_key_gap_over_window": 0.0}
     for (bb, h), r in oracle.items():
@@ -107,32 +130,35 @@ def compare_masks(gpu_mask: np.ndarray, oracle: dict, p: float, causal: bool) ->
         nb = o.shape[0]
         stats["blocks"] += nb * (nb + 1) // 2 if causal else nb * nb
         diff = np.argwhere(g != o)
+        dec = decisions(r, merge)
         for i in np.unique(diff[:, 0]) if diff.size else []:
             J = po.admissible(int(i), nb, causal)
             cols = diff[diff[:, 0] == i, 1]
-            br = {z: _branch_excuses(r[f"S_{z}"], r[f"L_{z}"], r[f"m_{z}"], int(i), J, p) for z in ("high", "low")}
-            win = key_tie_window(r["L_high"][i, J]), key_tie_window(r["L_low"][i, J])
+            br = {name: _branch_excuses(S, L, m, int(i), J, p) for name, S, L, m in dec}
+            win = {name: key_tie_window(L[i, J]) for name, S, L, m in dec}
             for j in cols:
                 stats["mismatch"] += 1
                 if j >= len(J):  # outside the admissible range: never excusable
                     stats["unexcused"] += 1
                     stats["where"].append((bb, h, int(i), int(j)))
                     continue
-                if o[i, j]:  # oracle keeps it, the GPU drops it in every branch
-                    need = [z for z in ("high", "low") if r[f"m_{z}"][i, j]]
-                    ok = lambda f: all(f(z) for z in need)
-                else:        # the oracle drops it, the GPU keeps it in some branch
-                    need = ["high", "low"]
-                    ok = lambda f: any(f(z) for z in need)
-                if ok(lambda z: br[z][0][j]):
+                kept_by = [name for name, S, L, m in dec if m[i, j]]
+                dropped_by = [name for name, S, L, m in dec if not m[i, j]]
+                if merge == "mix":
+                    need, ok = ["mix"], all
+                elif merge == "intersect":
+                    need, ok = (list(br), any) if o[i, j] else (dropped_by, all)
+                else:
+                    need, ok = (kept_by, all) if o[i, j] else (list(br), any)
+                if ok(br[z][0][j] for z in need):
                     stats["mass_tie"] += 1
-                elif ok(lambda z: br[z][0][j] or br[z][1][j]):
+                elif ok(br[z][0][j] or br[z][1][j] for z in need):
                     stats["score_tie"] += 1
-                    for zi, z in enumerate(("high", "low")):
-                        if z in need and br[z][1][j] and not br[z][0][j]:
+                    for z in need:
+                        if br[z][1][j] and not br[z][0][j]:
                             stats["max_key_gap"] = max(stats["max_key_gap"], float(br[z][2][j]))
                             stats["max_key_gap_over_window"] = max(stats["max_key_gap_over_window"],
-                                                                    float(br[z][2][j]) / win[zi])
+                                                                    float(br[z][2][j]) / win[z])
                 else:
                     stats["unexcused"] += 1
                     stats["where"].append((bb, h, int(i), int(j)))

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 5
+    assert lib.prism_abi_version() == 6
     for s in range(11):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
@@ -169,6 +169,15 @@ E = _abi
     (dict(c=cfg(block_size=64)), E.ERR_UNSUPPORTED),
     (dict(q=tensor(seq=8193 * 128), k=tensor(seq=8193 * 128, heads=8), m=mask(seq=8193 * 128)), E.ERR_UNSUPPORTED),
     (dict(m=mask(format=2)), E.ERR_CONFIG),
+    (dict(c=cfg(merge=3)), E.ERR_CONFIG),
+    (dict(c=cfg(merge=-1)), E.ERR_CONFIG),
+    (dict(c=cfg(band_mode=2)), E.ERR_CONFIG),
+    (dict(c=cfg(band_mode=1, d_high=56)), E.ERR_CONFIG),     # adaptive bands move in 16-dim steps
+    (dict(c=cfg(band_mode=1, d_low=88)), E.ERR_CONFIG),
+    (dict(c=cfg(band_mode=1, tau_mode=3)), E.ERR_CONFIG),    # per-vector temperature: static bands only
+    # the mixture merge runs on the fused path (up to 1024 blocks)
+    (dict(q=tensor(seq=1025 * 128), k=tensor(seq=1025 * 128, heads=8), m=mask(seq=1025 * 128),
+          c=cfg(merge=2)), E.ERR_UNSUPPORTED),
     # launch limits: a second grid dimension of 65536, 2^32 work-items
     (dict(q=tensor(batch=65536, heads=1, seq=128), k=tensor(batch=65536, heads=1, seq=128),
           m=mask(seq=128, heads=1, batch=65536)), E.ERR_UNSUPPORTED),
@@ -321,3 +330,22 @@ def test_noalloc_scratch_limit(lib):
     assert noalloc(lib, q3, k3, cfg(workspace=0), mask(seq=2048 * 128)) == E.ERR_SCRATCH
     # the inspection copy of the logits counts too
     assert noalloc(lib, q, k, cfg(workspace=0, flags=E.EST_KEEP_LOGITS), mask(seq=131072, heads=64)) == E.ERR_SCRATCH
+
+
+def test_adaptive_layout_sections(lib):
+    """adaptive bands add a pooled-spectrum section (fp64, a value per RoPE pair of
+    every query and KV head) and a per-head split section (4 int32) after the logits"""
+    q, k = tensor(seq=1000, heads=32), tensor(seq=1000, heads=8)
+    L = PrismWorkspaceLayout()
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg()),
+                                               ctypes.byref(L)) == 0
+    static_total = L.total_bytes
+    assert L.spectrum_offset == L.split_offset == L.total_bytes  # empty sections
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(band_mode=1)),
+                                               ctypes.byref(L)) == 0
+    assert L.spectrum_offset == static_total and L.spectrum_offset % 256 == 0
+    assert L.split_offset >= L.spectrum_offset + (32 + 8) * 64 * 8 and L.split_offset % 256 == 0
+    assert L.total_bytes >= L.split_offset + 32 * 16 and L.total_bytes % 256 == 0
+    for merge in (1, 2):
+        assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(merge=merge))) \
+            == static_total

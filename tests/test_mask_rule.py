@@ -7,7 +7,7 @@ import oracle.prism_oracle as po
 from tests.parity import KEY_ULP, LOG2E, LOGIT_TOL_REL, compare_masks, key_tie_window
 
 
-def oracle_dict(L_high, L_low, p):
+def oracle_dict(L_high, L_low, p, merge="union"):
     """one head's oracle results for given band logits (natural units), causal"""
     nb = L_high.shape[0]
     r = {}
@@ -21,11 +21,11 @@ def oracle_dict(L_high, L_low, p):
             S[i, J] = e / e.sum()
         r[f"L_{z}"], r[f"S_{z}"] = Lm, S
         r[f"m_{z}"] = po.top_p_mask(S, p, True)
-    r["mask"] = po.union(r["m_high"], r["m_low"])
+    r["mask"] = po.merge_masks(r, p, True, merge)
     return {(0, 0): r}
 
 
-def row_case(delta, p=None, low_peaked=True):
+def row_case(delta, p=None, low_peaked=True, merge="union"):
     """8 key blocks; the high branch's last row has logits whose ranks 3 and 4
     differ by delta; p keeps ranks 0..3 there unless given"""
     nb = 8
@@ -39,7 +39,7 @@ def row_case(delta, p=None, low_peaked=True):
         e = np.exp(Lh[7] - 2.0)
         cum = np.cumsum(e / e.sum())
         p = float((cum[2] + cum[3]) / 2)
-    return oracle_dict(Lh, Ll, p), p
+    return oracle_dict(Lh, Ll, p, merge), p
 
 
 def swapped(orc, pairs):
@@ -114,3 +114,43 @@ def test_above_diagonal_never_excused():
     g[0, 0, 2, 5] = 1
     st = compare_masks(g, orc, p, True)
     assert st["unexcused"] == 1 and st["where"] == [(0, 0, 2, 5)]
+
+
+def test_intersection_rule():
+    """intersection: the high branch's rank 3/4 swap within the key window
+    (the low branch keeps both blocks) is excused on both blocks; outside
+    the window it fails"""
+    for delta, excused in ((1e-8, True), (1e-3, False)):
+        orc, p = row_case(delta, low_peaked=False, merge="intersect")
+        r = orc[(0, 0)]
+        if not (r["m_low"][7, 3] and r["m_low"][7, 4]):
+            pytest.skip("the low branch of this seeded row does not keep blocks 3 and 4")
+        assert r["mask"][7, 3] == 1 and r["mask"][7, 4] == 0
+        g = r["mask"].copy()[None, None]
+        g[0, 0, 7, 3], g[0, 0, 7, 4] = 0, 1
+        st = compare_masks(g, orc, p, True, merge="intersect")
+        assert st["mismatch"] == 2
+        assert (st["unexcused"] == 0) == excused, st
+
+
+def test_mixture_rule():
+    """mixture: one decision on (S_high + S_low) / 2; a swap of its boundary
+    pair within the key window is a key tie, a flip far above it fails"""
+    nb = 8
+    Lh = np.zeros((nb, nb))
+    Ll = np.zeros((nb, nb))
+    Lh[7] = [3.0, 2.0, 1.0, 0.0, 0.0, -1.0, -2.0, -3.0]
+    Ll[7] = [3.0, 2.0, 1.0, 0.0, -1e-8, -1.0, -2.0, -3.0]  # mixture ranks 3 and 4 nearly tie
+    S = 0.5 * (np.exp(Lh[7]) / np.exp(Lh[7]).sum() + np.exp(Ll[7]) / np.exp(Ll[7]).sum())
+    cum = np.cumsum(np.sort(S)[::-1])
+    p = float((cum[2] + cum[3]) / 2)
+    orc = oracle_dict(Lh, Ll, p, merge="mix")
+    r = orc[(0, 0)]
+    assert r["mask"][7, :4].all() and not r["mask"][7, 4:].any()
+    g = r["mask"].copy()[None, None]
+    g[0, 0, 7, 3], g[0, 0, 7, 4] = 0, 1
+    st = compare_masks(g, orc, p, True, merge="mix")
+    assert (st["mismatch"], st["score_tie"], st["unexcused"]) == (2, 2, 0)
+    g = r["mask"].copy()[None, None]
+    g[0, 0, 7, 0] = 0
+    assert compare_masks(g, orc, p, True, merge="mix")["unexcused"] == 1

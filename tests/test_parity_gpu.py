@@ -97,6 +97,24 @@ SMALL = {
     "mrope_video": ("qwen3_vl_8b_video_32k",
                     dict(seq=6000, hq=4, hkv=1, rope=Rope("mrope", mrope="interleaved", sections=(24, 20, 20),
                                                           grid=(2, 16, 48))), {}, "bshd", "interleaved"),
+    # the merge variants and per-head adaptive bands (the weaknesses the review lists)
+    "merge_intersect": ("llama3_8b_32k", dict(seq=3000, hq=4, hkv=2), dict(merge="intersect"), "bshd", "interleaved"),
+    "merge_mix": ("llama3_8b_32k", dict(seq=3000, hq=4, hkv=2), dict(merge="mix"), "bshd", "interleaved"),
+    "merge_mix_noncausal": ("llama3_8b_32k", dict(seq=2500, hq=2, hkv=1, causal=False), dict(merge="mix"), "bshd",
+                            "interleaved"),
+    "adaptive_spectral": ("llama3_8b_spectral_32k", dict(seq=5000, hq=8, hkv=4), dict(band_mode="adaptive"), "bshd",
+                          "interleaved"),
+    "adaptive_half_unit_mix": ("llama3_8b_spectral_32k", dict(seq=3000, hq=8, hkv=4),
+                               dict(band_mode="adaptive", tau_mode="unit", merge="mix"), "bshd", "half"),
+    "adaptive_gap_intersect": ("llama3_8b_spectral_32k", dict(seq=3000, hq=8, hkv=4),
+                               dict(band_mode="adaptive", d_high=32, d_low=64, merge="intersect"), "bshd",
+                               "interleaved"),
+    "adaptive_batch2_bhsd": ("llama3_8b_spectral_32k", dict(seq=2000, hq=4, hkv=2, batch=2),
+                             dict(band_mode="adaptive", tau_mode="none"), "bhsd", "interleaved"),
+    "adaptive_nb_1100": ("llama3_8b_spectral_32k", dict(seq=1100 * 128 - 9, hq=4, hkv=2),
+                         dict(band_mode="adaptive"), "bshd", "interleaved"),
+    "intersect_nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128, hq=2, hkv=1), dict(merge="intersect"), "bshd",
+                          "interleaved"),
 }
 
 
@@ -118,8 +136,19 @@ def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=
         torch.cuda.synchronize()
         assert np.array_equal(plain.cpu().numpy(), gm)
     orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
-                                causal=cfg.causal, rope_layout=rope_layout, tau_mode=cfg.tau_mode)
+                                causal=cfg.causal, rope_layout=rope_layout, tau_mode=cfg.tau_mode, merge=cfg.merge,
+                                band_mode=cfg.band_mode)
     assert set(np.unique(gm)) <= {0, 1}
+    if cfg.band_mode == "adaptive":
+        # every head's split, as the oracle chooses it
+        split = ws[L.split_offset: L.split_offset + w.batch * w.hq * 16].view(torch.int32).reshape(
+            w.batch, w.hq, 4).cpu().numpy()
+        got = {key: tuple(split[key[0], key[1], 2:].tolist()) for key in orc}
+        want = {key: tuple(int(x) for x in r["bands"]) for key, r in orc.items()}
+        say(f"    adaptive bands (d_high, d_low) per head: {[got[key] for key in sorted(got)]}")
+        assert got == want
+        for key, (dh, dl) in want.items():
+            assert tuple(split[key[0], key[1], :2].tolist()) == (min(dh, 128 - dl), max(dh, 128 - dl))
     if cfg.causal:
         assert not np.triu(gm, 1).any()
     if check_stages:
@@ -143,7 +172,7 @@ def run_estimator_case(name, base, over, cov, layout, rope_layout, check_stages=
                 worst = max(worst, err_rel)
                 assert err_rel <= LOGIT_TOL_REL, (bb, h, z, err_abs, err_rel)
         say(f"    logits: max per-row relative error {worst:.2e} (bound {LOGIT_TOL_REL:.0e})")
-    st = compare_masks(gm, orc, cfg.p, cfg.causal)
+    st = compare_masks(gm, orc, cfg.p, cfg.causal, merge=cfg.merge)
     dens = gm.sum() / max(1, st["blocks"])
     say(f"    density={dens:.4f} blocks={st['blocks']} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
         f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
@@ -324,6 +353,7 @@ LONG = {
     "nb_2100_p_one": ("llama3_8b_32k", dict(seq=2100 * 128, hq=1, hkv=1), dict(p=1.0)),
     "nb_8192_max": ("llama3_8b_32k", dict(seq=8192 * 128, hq=1, hkv=1), dict()),  # 1,048,576 tokens, the largest
     "nb_2100_fp32": ("tiny_fp32_2k", dict(seq=2100 * 128 - 3, hq=1, hkv=1), dict()),
+    "nb_2100_intersect": ("llama3_8b_32k", dict(seq=2100 * 128, hq=1, hkv=1), dict(merge="intersect")),
 }
 
 
@@ -342,8 +372,8 @@ def test_long_rows(name):
     gm = m8.cpu().numpy()
     assert np.array_equal(mb.cpu().numpy(), pack_bits(gm))
     orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
-                                causal=cfg.causal)
-    st = compare_masks(gm, orc, cfg.p, cfg.causal)
+                                causal=cfg.causal, merge=cfg.merge)
+    st = compare_masks(gm, orc, cfg.p, cfg.causal, merge=cfg.merge)
     say(f"    density={gm.sum() / max(1, st['blocks']):.4f} mismatch={st['mismatch']} mass_tie={st['mass_tie']} "
         f"score_tie={st['score_tie']} unexcused={st['unexcused']} {st['where'][:5]}")
     record_parity(f"long:{name}", st)
