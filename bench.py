@@ -20,6 +20,7 @@ is reported too. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -309,6 +310,27 @@ def main():
         est_w.append(ev[0].elapsed_time(ev[1]))
     est_written_flush_ms = float(np.median(est_w))
 
+    # context: the same estimator as one persistent launch (grid barrier instead of kernel
+    # boundaries), read-flushed like the timed steps; its mask must equal theirs bit for bit
+    single = None
+    if nb <= 1024:
+        cfg1 = dataclasses.replace(cfg, single_launch=True)
+        ws1 = prism.new_workspace(qd, kd, cfg1)
+        m1 = torch.empty_like(mask)
+        ts = []
+        for i in range(args.warmup + args.steps):
+            flush()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record()
+            prism.estimate(qd, kd, cfg1, workspace=ws1, mask_out=m1)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                ts.append(ev[0].elapsed_time(ev[1]))
+        single = {"estimator_ms": round(float(np.median(ts)), 3), "mask_identical": bool(torch.equal(m1, mask))}
+        log(f"single-launch estimator: {single}")
+        del ws1, m1
+
     # the sparse output as stored, kept on the host before the dense baselines overwrite `out`
     out_bits = (out.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16"
                 else out.cpu().numpy()) if not args.no_cpu_baseline else None
@@ -334,6 +356,7 @@ def main():
                    "mask_format": "bits" if args.mask_bits else "u8"},
         "estimator_ms": round(est_ms, 3), "attention_ms": round(attn_ms, 3),
         "estimator_ms_after_written_flush": round(est_written_flush_ms, 3),
+        "estimator_single_launch": single,
         "wall_ms_per_step_incl_cache_flush": round(wall_ms, 3),
         "mask_density": round(density, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -42,6 +42,7 @@ class EstimatorConfig:
     keep_logits: bool = False  # also store the band logits in the workspace (inspection)
     merge: str = "union"       # "union" (the pages' step 7), "intersect" or "mix"
     band_mode: str = "static"  # "static" (the pages' split) or "adaptive" (per head)
+    single_launch: bool = False  # the whole estimator as one persistent kernel (grid barrier)
 
 
 def _torch():
@@ -87,7 +88,9 @@ def _cfg(cfg: EstimatorConfig, workspace=None) -> PrismCfg:
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return PrismCfg(cfg.block_size, cfg.d_high, cfg.d_low, cfg.p, int(bool(cfg.causal)), _ROPE[cfg.rope_layout],
-                    _TAU[cfg.tau_mode], _abi.EST_KEEP_LOGITS if cfg.keep_logits else 0, _MERGE[cfg.merge],
+                    _TAU[cfg.tau_mode],
+                    (_abi.EST_KEEP_LOGITS if cfg.keep_logits else 0) | (_abi.EST_SINGLE_LAUNCH if cfg.single_launch else 0),
+                    _MERGE[cfg.merge],
                     _BANDS[cfg.band_mode], ws_ptr, ws_bytes)
 
 

@@ -12,7 +12,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
 
-PRISM_ABI_VERSION = 6
+PRISM_ABI_VERSION = 7
 
 # prism_status_t
 (OK, ERR_NULL, ERR_DTYPE, ERR_SHAPE, ERR_STRIDE, ERR_ALIGN, ERR_CONFIG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_LAUNCH,
@@ -28,6 +28,8 @@ MASK_U8, MASK_BITS = 0, 1
 MERGE_UNION, MERGE_INTERSECT, MERGE_MIX = 0, 1, 2
 BANDS_STATIC, BANDS_ADAPTIVE = 0, 1
 EST_KEEP_LOGITS = 1
+EST_SINGLE_LAUNCH = 2
+SINGLE_MAX_WGS = 4096  # barrier words in the workspace's barrier section
 
 
 class PrismTensor(ctypes.Structure):
@@ -63,7 +65,7 @@ class PrismWorkspaceLayout(ctypes.Structure):
         ("logits_plane", ctypes.c_int64), ("spectrum_offset", ctypes.c_size_t), ("split_offset", ctypes.c_size_t),
         ("total_bytes", ctypes.c_size_t),
         ("nb", ctypes.c_int64), ("seg_lo", ctypes.c_int32), ("seg_hi", ctypes.c_int32),
-        ("overlap", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("overlap", ctypes.c_int32), ("reserved", ctypes.c_int32), ("barrier_offset", ctypes.c_size_t),
     ]
 
 

@@ -1,6 +1,8 @@
 // C ABI of libprism: argument validation, workspace layout and launch order.
 // Every check below runs on the host before the first HIP call of an entry
 // point; a failed check returns its status with nothing enqueued.
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 
@@ -85,7 +87,7 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if (cfg->causal != 0 && cfg->causal != 1) return PRISM_ERR_CONFIG;
   if (cfg->rope_layout != PRISM_ROPE_INTERLEAVED && cfg->rope_layout != PRISM_ROPE_HALF) return PRISM_ERR_CONFIG;
   if (cfg->tau_mode < PRISM_TAU_FULLSPEC || cfg->tau_mode > PRISM_TAU_PERVEC) return PRISM_ERR_CONFIG;
-  if (cfg->flags & ~PRISM_EST_KEEP_LOGITS) return PRISM_ERR_CONFIG;
+  if (cfg->flags & ~(PRISM_EST_KEEP_LOGITS | PRISM_EST_SINGLE_LAUNCH)) return PRISM_ERR_CONFIG;
   if (cfg->merge < PRISM_MERGE_UNION || cfg->merge > PRISM_MERGE_MIX) return PRISM_ERR_CONFIG;
   if (cfg->band_mode != PRISM_BANDS_STATIC && cfg->band_mode != PRISM_BANDS_ADAPTIVE) return PRISM_ERR_CONFIG;
   if (cfg->band_mode == PRISM_BANDS_ADAPTIVE &&
@@ -95,6 +97,11 @@ int check_cfg(const prism_cfg_t *cfg, int64_t seq) {
   if ((seq + kBlock - 1) / kBlock > kMaxBlocks) return PRISM_ERR_UNSUPPORTED;
   // the mixture merge selects both branches' rows in one wave: fused path only
   if (cfg->merge == PRISM_MERGE_MIX && (seq + kBlock - 1) / kBlock > prism::kFusedMaxBlocks)
+    return PRISM_ERR_UNSUPPORTED;
+  // one launch: the fused scores and selection, and one grid barrier (no
+  // spectrum and split phases)
+  if ((cfg->flags & PRISM_EST_SINGLE_LAUNCH) &&
+      ((seq + kBlock - 1) / kBlock > prism::kFusedMaxBlocks || cfg->band_mode != PRISM_BANDS_STATIC))
     return PRISM_ERR_UNSUPPORTED;
   return PRISM_OK;
 }
@@ -123,6 +130,8 @@ void make_layout(const prism_tensor_t *q, const prism_tensor_t *k, const prism_c
   const bool adaptive = cfg->band_mode == PRISM_BANDS_ADAPTIVE;
   L->spectrum_offset = off; off = round_up(off + (adaptive ? b * (q->heads + k->heads) * (kHeadDim / 2) * 8 : 0), 256);
   L->split_offset = off;    off = round_up(off + (adaptive ? b * q->heads * 16 : 0), 256);
+  const bool single = cfg->flags & PRISM_EST_SINGLE_LAUNCH;
+  L->barrier_offset = off;  off = round_up(off + (single ? prism::kSingleTauOffset + b * q->heads * 16 : 0), 256);
   L->total_bytes = off;
   L->nb = nb;
   const int lo_start = kHeadDim - cfg->d_low;
@@ -137,6 +146,16 @@ int check_mask_format(const prism_mask_t *m) {
   if (m->format != PRISM_MASK_U8 && m->format != PRISM_MASK_BITS) return PRISM_ERR_CONFIG;
   if (reinterpret_cast<uintptr_t>(m->data) % (m->format == PRISM_MASK_U8 ? 16 : 4)) return PRISM_ERR_ALIGN;
   return PRISM_OK;
+}
+
+// A value for the single-launch estimator's barrier words that no earlier
+// call of this process wrote (and, seeded from the clock, that a stale
+// workspace is unlikely to hold): odd, distinct per call.
+uint64_t barrier_tag() {
+  static const uint64_t seed =
+      (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull;
+  static std::atomic<uint64_t> calls{0};
+  return (seed + 2 * calls.fetch_add(1, std::memory_order_relaxed)) | 1u;
 }
 
 prism::TensorArg targ(const prism_tensor_t *t) {
@@ -283,6 +302,24 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   }
   ta.h0 = 0;
   ta.nh = ta.hq;
+  sc.h0 = tp.h0 = 0;
+  sc.nh = tp.nh = ta.hq;
+  if (cfg->flags & PRISM_EST_SINGLE_LAUNCH) {
+    prism::SingleParams P;
+    P.pa = pa;
+    P.ta = ta;
+    P.sa = sc;
+    P.tp = tp;
+    P.g.slots = reinterpret_cast<uint64_t *>(ws + L.barrier_offset);
+    P.g.status = reinterpret_cast<int32_t *>(ws + L.barrier_offset + prism::kSingleStatusOffset);
+    P.g.ticket = reinterpret_cast<uint64_t *>(ws + L.barrier_offset + prism::kSingleTicketOffset);
+    P.g.go = reinterpret_cast<uint64_t *>(ws + L.barrier_offset + prism::kSingleGoOffset);
+    P.g.tau_words = reinterpret_cast<uint64_t *>(ws + L.barrier_offset + prism::kSingleTauOffset);
+    P.g.tag = barrier_tag();
+    P.batch = (int)q->batch;
+    const hipError_t e = prism::launch_estimate_single(P, fp32, prism::kSingleMaxWgs, s);
+    return e == hipSuccess ? PRISM_OK : PRISM_ERR_LAUNCH;
+  }
   if (prism::launch_pool(pa, (int)q->batch, fp32, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   if (adaptive) {
     prism::SpectrumArgs sa;
@@ -306,8 +343,6 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   } else if (prism::launch_tau(ta, (int)q->batch, s) != hipSuccess) {
     return PRISM_ERR_LAUNCH;
   }
-  sc.h0 = tp.h0 = 0;
-  sc.nh = tp.nh = ta.hq;
   if (nb <= prism::kFusedMaxBlocks) {
     if (prism::launch_score_topp(sc, tp, s) != hipSuccess) return PRISM_ERR_LAUNCH;
   } else {

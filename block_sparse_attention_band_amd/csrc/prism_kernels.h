@@ -111,6 +111,36 @@ hipError_t launch_topp(const TopPArgs &a, hipStream_t s);
 // both at once, logits kept on chip (nb <= kFusedMaxBlocks)
 hipError_t launch_score_topp(const ScoreArgs &sc, const TopPArgs &tp, hipStream_t s);
 
+// The estimator in one persistent launch (nb <= kFusedMaxBlocks, static
+// bands): its grid-wide barrier words and status.
+struct SingleArgs {
+  uint64_t *slots;         // one barrier word per workgroup (any prior contents)
+  int32_t *status;         // set to 1 when a workgroup gave up waiting
+  uint64_t *ticket;        // the strips' ticket counter: (tag low 32 bits << 32) | next strip
+  uint64_t *go;            // kGoCopies words kGoStride apart, := tag once every workgroup has reached the barrier
+  uint64_t *tau_words;     // [batch * Hq][2]: tau_high, tau_low as (tag low 32 bits << 32) | float bits
+  uint64_t tag;            // this call's value, unlike any earlier call's (odd)
+};
+constexpr int kSingleMaxWgs = 4096;  // barrier words in the workspace
+constexpr int kGoCopies = 16, kGoStride = 32;  // go words: 16 copies, 256 bytes apart
+// the barrier section: kSingleMaxWgs barrier words, the status word (8 bytes
+// with padding), the ticket counter, the go words (from a 256-byte boundary),
+// then two words per query head
+constexpr size_t kSingleStatusOffset = kSingleMaxWgs * 8;
+constexpr size_t kSingleTicketOffset = kSingleStatusOffset + 8;
+constexpr size_t kSingleGoOffset = kSingleStatusOffset + 256;
+constexpr size_t kSingleTauOffset = kSingleGoOffset + kGoCopies * kGoStride * 8;
+
+struct SingleParams {
+  PoolArgs pa;
+  TauArgs ta;
+  ScoreArgs sa;
+  TopPArgs tp;
+  SingleArgs g;
+  int32_t batch;
+};
+hipError_t launch_estimate_single(const SingleParams &p, int fp32, int grid_cap, hipStream_t s);
+
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
   TensorArg q, k, v, o;
@@ -139,5 +169,8 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
 hipError_t stream_device(hipStream_t s, int *dev);
 // Compute units of a device, queried once per device and cached.
 hipError_t device_cu_count(int dev, int *cus);
+// Workgroups of `threads` threads of kernel f resident per CU (on the current
+// device; every device this library runs on is a gfx950), cached per kernel.
+hipError_t kernel_occupancy(const void *f, int threads, int *per_cu);
 
 }  // namespace prism

@@ -20,11 +20,15 @@
 //   branches go through the workspace's logit planes (64 x 64 tiles on fp32
 //   MFMA 32x32x2), then one wave per row and branch reads its row once into
 //   registers (32, 64 or 128 logits per lane) and selects.
+// estimate_single_kernel (rows of at most 1024 blocks, static bands): the
+//   whole estimator in one persistent launch -- the pooling pass, a grid-wide
+//   barrier, then per strip the head's temperatures and score_topp's work --
+//   with the multi-kernel path's arithmetic, so both give the same bits.
 // In every score kernel the canonical dims split into three segments,
 //   high-only / middle / low-only, each dim entering one segment's dot
 //   product once; L_high = (s0 + s1) c_high and L_low = (s1 + s2) c_low (the
 //   middle segment only when the bands overlap), in log2 units.
-#include "prism_kernels.h"
+#include "pool_device.h"
 
 namespace prism {
 namespace {
@@ -698,22 +702,26 @@ constexpr int kFusedChunk = 256;       // key blocks per score chunk
 constexpr int kFusedPitch = kFusedChunk + 4;
 constexpr int kRuntime16 = 100;
 
-template <int LO16, int HI16, bool PV, bool MIX>
-__global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
-void score_topp_kernel(ScoreArgs a, TopPArgs t) {
-  __shared__ __attribute__((aligned(16))) float lt[2][kStrip][kFusedPitch];  // [branch][row][key]
-  __shared__ __attribute__((aligned(16))) float4 qs[kStrip * 32];           // Qbar rows, 16-byte slots swizzled
-  __shared__ unsigned long long bins_s[kFusedWaves][kBinSlots];
+// LDS of one strip: both branches' logits of a 256-block chunk, the strip's
+// Qbar rows, and each wave's selection histogram.
+struct FusedLds {
+  float lt[2][kStrip][kFusedPitch];                // [branch][row][key]
+  float4 qs[kStrip * 32];                          // Qbar rows, 16-byte slots swizzled
+  unsigned long long bins_s[kFusedWaves][kBinSlots];
+};
 
-  const int nI = (a.nb + kStrip - 1) / kStrip;
-  const int nbh = a.batch * a.nh;
-  const int lbh = blockIdx.x % nbh;
-  const int rank = blockIdx.x / nbh;
-  const int I = a.causal ? nI - 1 - rank : rank;  // longest strips first
-  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+// Strip I (query blocks 16 I .. 16 I + 15) of head bh = b * Hq + h, with the
+// head's branch temperatures tau_h, tau_l; every thread of the 8-wave
+// workgroup calls it (it holds barriers).
+template <int LO16, int HI16, bool PV, bool MIX, typename AfterScores>
+__device__ __forceinline__ void score_topp_strip(ScoreArgs a, const TopPArgs &t, int I, int bh, float tau_h,
+                                                 float tau_l, FusedLds &L, int tid, AfterScores &&after_scores) {
+  auto &lt = L.lt;
+  auto &qs = L.qs;
+  auto &bins_s = L.bins_s;
   head_bands(a, bh);
   const int b = bh / a.hq, h = bh % a.hq, gk = h / (a.hq / a.hkv);
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = I * kStrip;
   const int ncol = a.causal ? min(a.nb, q0 + kStrip) : a.nb;  // key blocks any row of the strip admits
@@ -728,9 +736,8 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   }
 
   const float kLog2e = 1.4426950408889634f;
-  const float *tau = a.tau + (int64_t)bh * 8;
-  const float ch = kLog2e / (tau[0] * sqrtf((float)a.d_high));
-  const float cl = kLog2e / (tau[1] * sqrtf((float)a.d_low));
+  const float ch = kLog2e / (tau_h * sqrtf((float)a.d_high));
+  const float cl = kLog2e / (tau_l * sqrtf((float)a.d_low));
   float fqh = 1.f, fql = 1.f;  // per-vector factors of this lane's query block
   if constexpr (PV) {
     const float4 e = *reinterpret_cast<const float4 *>(a.qsq + ((int64_t)bh * a.nb + min(q0 + r16, a.nb - 1)) * 4);
@@ -871,6 +878,7 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
     }
     __syncthreads();  // every wave has read the chunk before the next one is stored
   }
+  after_scores();
 
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -888,6 +896,302 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
   }
 }
 
+// One workgroup per (strip, head), longest strips first.
+template <int LO16, int HI16, bool PV, bool MIX>
+__global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void score_topp_kernel(ScoreArgs a, TopPArgs t) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[sizeof(FusedLds)];
+  const int nI = (a.nb + kStrip - 1) / kStrip;
+  const int nbh = a.batch * a.nh;
+  const int lbh = blockIdx.x % nbh;
+  const int rank = blockIdx.x / nbh;
+  const int I = a.causal ? nI - 1 - rank : rank;
+  const int bh = (lbh / a.nh) * a.hq + a.h0 + lbh % a.nh;
+  const float *tau = a.tau + (int64_t)bh * 8;
+  score_topp_strip<LO16, HI16, PV, MIX>(a, t, I, bh, tau[0], tau[1], *reinterpret_cast<FusedLds *>(smem), threadIdx.x,
+                                        [] {});
+}
+
+
+// ---- the whole estimator in one launch (rows of at most 1024 blocks)
+//
+// A persistent grid of 8-wave workgroups, all resident at once (cooperative
+// launch), runs the work of the multi-kernel path with one grid-wide barrier
+// in place of the kernel boundaries:
+//  (1)-(3) pooling: the first 256 threads of each workgroup pool work items
+//    exactly as pool_kernel does (pool_device.h), the results of up to
+//    kSingleSlots items waiting in LDS until their reads are done (the other
+//    waves only join the barriers: eight streaming waves per CU read faster
+//    than sixteen);
+//  barrier: every workgroup publishes its writes (release at device scope,
+//    then its own barrier word := this call's tag) and waits until every
+//    word holds the tag (acquire at device scope);
+//  (4) temperatures: workgroup w computes those of head w, w + G, ...
+//    (tau_reduce, the tau kernel's arithmetic), writes them to the workspace
+//    and publishes tau_high and tau_low each in a 64-bit word beside the low
+//    32 bits of the tag (one atomic store each, so a reader that sees the
+//    tag sees the value: no fence and no cache invalidation on either side);
+//  (5)-(7) strips: taken from a ticket counter in the order the fused kernel's
+//    grid has (longest strips first, heads fastest), so that a workgroup
+//    that finishes early takes the next strip; per strip the head's two
+//    temperatures are read from their words, then score_topp_strip.
+// No word has to start at zero (the counter is set by workgroup 0 before the
+// barrier; the other words are recognised by the tag), so the call needs no
+// clearing launch. Every wait gives up after about 4 s (then `status` := 1
+// and the call's outputs are not valid).
+constexpr int kSingleSlots = 6;
+constexpr uint64_t kWaitTicks = 400000000ull;  // s_memrealtime ticks at 100 MHz: 4 s
+
+template <bool FP32>
+struct SinglePoolLds {
+  static constexpr int E = Elem<FP32>::E;
+  float red[kPoolThreads * E];                                  // token-parallel partial sums
+  float4 means[kSingleSlots][kPoolThreads * E / 4];            // E means per thread, per item
+  float4 energy[kSingleSlots][kPoolThreads / (kHeadDim / E)];  // three segment energies per head row
+};
+struct TauLds {
+  double red[6][kPoolThreads];
+  float out[8];
+};
+constexpr size_t kSingleLdsBytes = sizeof(SinglePoolLds<false>) > sizeof(FusedLds)
+                                       ? (sizeof(SinglePoolLds<false>) > sizeof(TauLds) ? sizeof(SinglePoolLds<false>)
+                                                                                         : sizeof(TauLds))
+                                       : (sizeof(FusedLds) > sizeof(TauLds) ? sizeof(FusedLds) : sizeof(TauLds));
+static_assert(sizeof(SinglePoolLds<true>) <= kSingleLdsBytes, "fp32 pooling LDS");
+static_assert(kSingleLdsBytes <= 80 * 1024 - 64, "two workgroups per CU");
+
+template <bool FP32>
+__device__ __forceinline__ void single_pool(const PoolArgs &a, int batch, unsigned char *smem) {
+  constexpr int E = Elem<FP32>::E;
+  constexpr int TPH = kHeadDim / E;
+  auto &L = *reinterpret_cast<SinglePoolLds<FP32> *>(smem);
+  const int tid = threadIdx.x;
+  const bool worker = tid < kPoolThreads;
+  const int per = pool_items(a);
+  const int all = batch * per, G = gridDim.x;  // < 2^31: at most 1024 blocks and 2^20 heads in all
+  for (int first = blockIdx.x; first < all; first += kSingleSlots * G) {
+    int nst = 0;
+    for (int gi = first; gi < all && nst < kSingleSlots; gi += G, ++nst) {
+      // batch entry and item, uniform (scalar registers: the addresses below stay scalar + lane offset)
+      const int b = __builtin_amdgcn_readfirstlane(gi / per), item = __builtin_amdgcn_readfirstlane(gi % per);
+      const PoolItem<FP32> w(a, item, worker ? tid : 0);
+      float acc[E];
+      if (worker) {
+        pool_accum<FP32>(a, b, w, acc);
+        pool_red_put<FP32>(w, tid, acc, L.red);
+      }
+      if (w.tokp > 1) __syncthreads();
+      if (worker) {
+        float st[E + 3];
+        pool_finish<FP32>(a, w, tid, acc, L.red, st);
+#pragma unroll
+        for (int e = 0; e < E; e += 4) L.means[nst][(tid * E + e) / 4] = make_float4(st[e], st[e + 1], st[e + 2], st[e + 3]);
+        if (w.tp == 0 && w.dg == 0) L.energy[nst][tid / TPH] = make_float4(st[E], st[E + 1], st[E + 2], 0.f);
+      }
+      __syncthreads();  // `red` is reused by the next item
+    }
+    if (worker) {
+      for (int k = 0; k < nst; ++k) {
+        const int gi = first + k * G;
+        const int b = __builtin_amdgcn_readfirstlane(gi / per), item = __builtin_amdgcn_readfirstlane(gi % per);
+        const PoolItem<FP32> w(a, item, tid);
+        const float4 en = L.energy[k][tid / TPH];
+        const float e3[3] = {en.x, en.y, en.z};
+        pool_write<FP32>(a, b, w, reinterpret_cast<const float *>(&L.means[k][tid * E / 4]), e3);
+      }
+    }
+    __syncthreads();  // the slots are reused by the next round
+  }
+}
+
+__device__ __forceinline__ bool waited_too_long(uint64_t t0) {
+  return __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
+}
+
+// One round of the grid barrier: every workgroup sets its barrier word to
+// `v`; workgroup 0 waits until every word holds v, then sets the go words to
+// v; each of the others waits on one go word (one thread polling, about once
+// a microsecond; kGoCopies copies on separate lines, so no one memory channel
+// takes every poll). `before_go` runs in workgroup 0 between the two.
+template <typename BeforeGo>
+__device__ __forceinline__ void barrier_round(const SingleArgs &g, uint64_t v, uint64_t t0, BeforeGo &&before_go) {
+  if (threadIdx.x == 0) __hip_atomic_store(g.slots + blockIdx.x, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (blockIdx.x == 0) {
+    for (;;) {
+      int ok = 1;
+      for (int w = threadIdx.x; w < (int)gridDim.x; w += blockDim.x)
+        ok &= __hip_atomic_load(g.slots + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == v;
+      if (__syncthreads_and(ok)) break;
+      if (__syncthreads_or(threadIdx.x == 0 && waited_too_long(t0))) {
+        if (threadIdx.x == 0) __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(32);
+    }
+    before_go();
+    if (threadIdx.x < kGoCopies)
+      __hip_atomic_store(g.go + threadIdx.x * kGoStride, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x == 0) {
+    const uint64_t *go = g.go + (blockIdx.x % kGoCopies) * kGoStride;
+    while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != v) {
+      if (waited_too_long(t0)) {
+        __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(32);
+    }
+  }
+  __syncthreads();
+}
+
+// The grid barrier after the pooling, in two rounds. Publishing to the other
+// XCDs takes a write-back of this XCD's L2 (the release at device scope);
+// issued by a workgroup while others still stream their pooling reads, those
+// write-backs slowed the reads by 13% (measured). So: round 1 only says that
+// this workgroup's stores have reached its L2 (tag); once every workgroup is
+// there, each writes its L2 back and says so (tag + 1), and after round 2
+// every workgroup invalidates its caches (the acquire at device scope).
+__device__ __forceinline__ void grid_barrier(const SingleArgs &g) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have reached the L2
+  __syncthreads();
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  barrier_round(g, g.tag, t0, [] {});
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  barrier_round(g, g.tag + 1, t0, [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); });
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
+}
+
+// a temperature published with the tag: (tag32 << 32) | float bits
+__device__ __forceinline__ uint64_t tagged(uint32_t tag32, float v) {
+  return ((uint64_t)tag32 << 32) | __float_as_uint(v);
+}
+
+// word i of the published temperatures, once it carries the tag (1 after
+// about 4 s without it, and status := 1)
+__device__ __forceinline__ float wait_tau(const SingleArgs &g, int i, uint32_t tag32) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint64_t v;
+  while (((v = __hip_atomic_load(g.tau_words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) != tag32) {
+    if (waited_too_long(t0)) {
+      __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return 1.f;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+  return __uint_as_float((uint32_t)v);
+}
+constexpr int kTauCache = 512;  // heads whose temperatures a workgroup keeps in LDS
+
+typedef const SingleParams __attribute__((address_space(4))) *ParamPtr;  // kernel-argument segment
+template <typename T>
+__device__ __forceinline__ T load_param(const T __attribute__((address_space(4))) *p) {
+  T v;
+  __builtin_memcpy(&v, (const T *)p, sizeof(T));
+  return v;
+}
+
+template <int LO16, int HI16, bool PV, bool MIX, bool FP32>
+__global__ __launch_bounds__(kFusedWaves * 64) __attribute__((amdgpu_waves_per_eu(4)))
+void estimate_single_kernel(SingleParams P) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSingleLdsBytes];
+  __shared__ int64_t ticket_s;
+  __shared__ float tau_s[2];
+  __shared__ float tau_cache[2 * kTauCache];
+  const uint32_t tag32 = (uint32_t)P.g.tag;
+  if (blockIdx.x == 0 && threadIdx.x == 0)  // tickets 0 .. G - 1 are taken implicitly (workgroup w: w)
+    __hip_atomic_store(P.g.ticket, ((uint64_t)tag32 << 32) | gridDim.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  single_pool<FP32>(P.pa, P.batch, smem);
+  grid_barrier(P.g);
+
+  auto &T = *reinterpret_cast<TauLds *>(smem);
+  auto &F = *reinterpret_cast<FusedLds *>(smem);
+  const int nbh = P.sa.batch * P.sa.nh;
+  for (int lbh = blockIdx.x; lbh < nbh; lbh += gridDim.x) {
+    const int bh = (lbh / P.sa.nh) * P.sa.hq + P.sa.h0 + lbh % P.sa.nh;
+    tau_reduce(P.ta, bh / P.sa.hq, bh % P.sa.hq, T.red, T.out);
+    __syncthreads();
+    if (threadIdx.x < 8) P.ta.tau[(int64_t)bh * 8 + threadIdx.x] = T.out[threadIdx.x];
+    if (threadIdx.x < 2)
+      __hip_atomic_store(P.g.tau_words + 2 * bh + threadIdx.x, tagged(tag32, T.out[threadIdx.x]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
+
+  // every head's temperatures into LDS (when they fit), once they are published
+  const bool cached = nbh <= kTauCache;
+  if (cached) {
+    for (int i = threadIdx.x; i < 2 * nbh; i += blockDim.x) {
+      const int lbh = i >> 1;
+      const int bh = (lbh / P.sa.nh) * P.sa.hq + P.sa.h0 + lbh % P.sa.nh;
+      tau_cache[i] = wait_tau(P.g, 2 * bh + (i & 1), tag32);
+    }
+    __syncthreads();
+  }
+
+  const int nI = (P.sa.nb + kStrip - 1) / kStrip;
+  const int64_t ntask = (int64_t)nI * nbh;
+  int64_t ticket = blockIdx.x;
+  int cur = -1;
+  float th = 1.f, tl = 1.f;
+  while (ticket < ntask) {
+    // The arguments (the kernel's only one, at the start of its argument
+    // segment) and the thread index are read through values opaque to the
+    // compiler in every strip, so it re-reads them there instead of holding
+    // them, and everything derived from them, in registers across the loop.
+    ParamPtr pp = (ParamPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(pp));
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const ScoreArgs sa = load_param(&pp->sa);
+    const TopPArgs tp = load_param(&pp->tp);
+    const SingleArgs g = load_param(&pp->g);
+    const int lbh = (int)(ticket % nbh), rank = (int)(ticket / nbh);
+    const int I = sa.causal ? nI - 1 - rank : rank;
+    const int bh = (lbh / sa.nh) * sa.hq + sa.h0 + lbh % sa.nh;
+    __syncthreads();  // the previous strip is done with the LDS and tau_s
+    if (cached) {
+      th = tau_cache[2 * lbh];
+      tl = tau_cache[2 * lbh + 1];
+    } else if (bh != cur) {  // this head's temperatures, once they are published
+      if (tid < 2) tau_s[tid] = wait_tau(g, 2 * bh + tid, tag32);
+      __syncthreads();
+      th = tau_s[0];
+      tl = tau_s[1];
+      cur = bh;
+    }
+    // the next ticket, taken once the strip's loads are done (a returning
+    // atomic in flight would hold up every wait for them)
+    uint64_t next = 0;
+    score_topp_strip<LO16, HI16, PV, MIX>(sa, tp, I, bh, th, tl, F, tid, [&] {
+      if (tid == 0) next = __hip_atomic_fetch_add(g.ticket, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+    if (tid == 0) {
+      // a counter without this call's tag was not set by this call: stop
+      ticket_s = (next >> 32) == tag32 ? (int64_t)(uint32_t)next : ntask;
+      if ((next >> 32) != tag32) __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    ticket = ticket_s;
+  }
+}
+
+template <int LO16, int HI16, bool PV, bool MIX>
+hipError_t launch_single_as(const SingleParams &P, int fp32, int grid_cap, hipStream_t s) {
+  const void *f = fp32 ? reinterpret_cast<const void *>(&estimate_single_kernel<LO16, HI16, PV, MIX, true>)
+                       : reinterpret_cast<const void *>(&estimate_single_kernel<LO16, HI16, PV, MIX, false>);
+  int per_cu = 0, cus = 0, dev = 0;
+  hipError_t e = stream_device(s, &dev);
+  if (e == hipSuccess) e = device_cu_count(dev, &cus);
+  if (e == hipSuccess) e = kernel_occupancy(f, kFusedWaves * 64, &per_cu);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const int G = min(per_cu * cus, grid_cap);
+  SingleParams p = P;
+  void *args[] = {&p};
+  return hipLaunchCooperativeKernel(f, dim3(G), dim3(kFusedWaves * 64), args, 0, s);
+}
 
 }  // namespace
 
@@ -941,6 +1245,27 @@ hipError_t launch_score_topp(const ScoreArgs &a, const TopPArgs &t, hipStream_t 
     hipLaunchKernelGGL((score_topp_kernel<-1, -1, false, false>), grid, block, 0, s, a, t);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_estimate_single(const SingleParams &P, int fp32, int grid_cap, hipStream_t s) {
+  const bool def = P.sa.seg_lo == 32 && P.sa.seg_hi == 64;
+  const bool by16 = P.sa.seg_lo % 16 == 0 && P.sa.seg_hi % 16 == 0;
+  if (P.tp.merge == PRISM_MERGE_MIX) {
+    if (P.sa.pervec) {
+      if (by16) return launch_single_as<kRuntime16, 0, true, true>(P, fp32, grid_cap, s);
+      return launch_single_as<-1, -1, true, true>(P, fp32, grid_cap, s);
+    }
+    if (by16) return launch_single_as<kRuntime16, 0, false, true>(P, fp32, grid_cap, s);
+    return launch_single_as<-1, -1, false, true>(P, fp32, grid_cap, s);
+  }
+  if (P.sa.pervec) {
+    if (def) return launch_single_as<2, 4, true, false>(P, fp32, grid_cap, s);
+    if (by16) return launch_single_as<kRuntime16, 0, true, false>(P, fp32, grid_cap, s);
+    return launch_single_as<-1, -1, true, false>(P, fp32, grid_cap, s);
+  }
+  if (def) return launch_single_as<2, 4, false, false>(P, fp32, grid_cap, s);
+  if (by16) return launch_single_as<kRuntime16, 0, false, false>(P, fp32, grid_cap, s);
+  return launch_single_as<-1, -1, false, false>(P, fp32, grid_cap, s);
 }
 
 hipError_t launch_topp(const TopPArgs &a, hipStream_t s) {

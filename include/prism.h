@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 6
+#define PRISM_ABI_VERSION 7
 
 typedef enum {
   PRISM_OK = 0,
@@ -145,8 +145,20 @@ typedef enum { PRISM_BANDS_STATIC = 0, PRISM_BANDS_ADAPTIVE = 1 } prism_band_mod
 /* Estimator flags (prism_cfg_t.flags). KEEP_LOGITS: also store both branches'
  * logits in the workspace (see logits_offset) for inspection. Sequences of at
  * most 1024 blocks otherwise keep them on chip: their scores and selection
- * run in one kernel, and the workspace has no logit planes. */
+ * run in one kernel, and the workspace has no logit planes.
+ * SINGLE_LAUNCH: run the whole estimator as one persistent kernel (a
+ * cooperative launch, every workgroup resident) with a grid-wide barrier
+ * between the pooling pass and the per-head temperatures, scores and
+ * selection, instead of three launches; same results, bit for bit. Needs at
+ * most 1024 blocks and PRISM_BANDS_STATIC (else PRISM_ERR_UNSUPPORTED). Its
+ * device-side words live in the workspace's barrier section (see
+ * barrier_offset); they are tagged with a value new to each call, so any
+ * prior contents are fine (a stale word matching that tag by chance, odds
+ * 2^-32 per word, would corrupt the call). The status word becomes 1 if a
+ * workgroup waited longer than about 4 s (the call's outputs are then not
+ * valid); the library never clears it. */
 #define PRISM_EST_KEEP_LOGITS 1
+#define PRISM_EST_SINGLE_LAUNCH 2
 
 typedef struct {
   int32_t block_size; /* B, tokens per block: 128 */
@@ -156,7 +168,7 @@ typedef struct {
   int32_t causal;     /* 1: query block i scores key blocks j <= i only */
   int32_t rope_layout;/* prism_rope_layout_t */
   int32_t tau_mode;   /* prism_tau_mode_t */
-  int32_t flags;      /* 0, or PRISM_EST_KEEP_LOGITS */
+  int32_t flags;      /* 0, or PRISM_EST_KEEP_LOGITS and/or PRISM_EST_SINGLE_LAUNCH */
   int32_t merge;      /* prism_merge_t (PRISM_MERGE_UNION: the pages' step (7)) */
   int32_t band_mode;  /* prism_band_mode_t (PRISM_BANDS_STATIC: the pages' split) */
   void *workspace;    /* device scratch, 256-byte aligned, >= prism_estimate_workspace_bytes() */
@@ -195,6 +207,11 @@ typedef struct {
   size_t total_bytes; /* == prism_estimate_workspace_bytes() */
   int64_t nb;         /* blocks per sequence, ceil(seq / block_size) */
   int32_t seg_lo, seg_hi, overlap, reserved;
+  size_t barrier_offset; /* PRISM_EST_SINGLE_LAUNCH: 4096 uint64 barrier words (one per
+                           workgroup), the int32 status word (padded to 8 bytes), a uint64
+                           counter of score tasks, at byte 33024 16 go words 256 bytes apart,
+                           then at byte 37120 two uint64 words per query head (batch * Hq)
+                           that publish its temperatures */
 } prism_workspace_layout_t;
 
 /* Version of this ABI (PRISM_ABI_VERSION). */
@@ -226,8 +243,8 @@ int prism_estimate_workspace_layout(const prism_tensor_t *q, const prism_tensor_
  * a per-head temperature reduction, and per query block the two band score
  * rows, their softmax, Top-P and the union. Scores and selection run in fp32.
  * Three kernels in order on `stream` for up to 1024 blocks (scores and
- * selection fused, logits on chip), four beyond (the logits pass through
- * the workspace). Every row, up to 8192 blocks, is selected from registers
+ * selection fused, logits on chip), or one with PRISM_EST_SINGLE_LAUNCH;
+ * four beyond (the logits pass through the workspace). Every row, up to 8192 blocks, is selected from registers
  * by the same radix select over fixed-point masses.
  * Deterministic: the same inputs give bit-identical masks and workspace. */
 int prism_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const prism_cfg_t *cfg,

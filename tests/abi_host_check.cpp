@@ -22,6 +22,12 @@ hipError_t launch_split(const SplitArgs &, int, hipStream_t) { ++g_launches; ret
 hipError_t launch_score(const ScoreArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_topp(const TopPArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_score_topp(const ScoreArgs &, const TopPArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
+SingleParams g_single;  // the last single-launch parameters
+hipError_t launch_estimate_single(const SingleParams &p, int, int grid_cap, hipStream_t) {
+  ++g_launches;
+  g_single = p;
+  return grid_cap >= 1 ? hipSuccess : hipErrorInvalidValue;
+}
 hipError_t launch_attn_bf16(const AttnArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_attn_fp32(const AttnArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t stream_device(hipStream_t, int *dev) { *dev = 0; return hipSuccess; }
@@ -100,6 +106,34 @@ int main() {
     CHECK(est(tensor(4096, 32), tensor(4096, 8), c, mask(4096, 32), 4) == PRISM_OK);
     CHECK(est(tensor(131073, 32), tensor(131073, 8), c, mask(131073, 32), 4) == PRISM_ERR_UNSUPPORTED);
   }
+  {  // one persistent launch: up to 1024 blocks, static bands; its barrier words in the workspace
+    prism_cfg_t c = cfg();
+    c.flags = PRISM_EST_SINGLE_LAUNCH;
+    prism_tensor_t q = tensor(131072, 32), k = tensor(131072, 8);
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_OK);
+    prism_workspace_layout_t L;
+    CHECK(prism_estimate_workspace_layout(&q, &k, &c, &L) == PRISM_OK);
+    CHECK(L.barrier_offset % 256 == 0 && L.total_bytes >= L.barrier_offset + 4096 * 8 + 4);
+    const char *ws = static_cast<const char *>(c.workspace);
+    CHECK(reinterpret_cast<const char *>(prism::g_single.g.slots) == ws + L.barrier_offset);
+    CHECK(reinterpret_cast<const char *>(prism::g_single.g.status) == ws + L.barrier_offset + 4096 * 8);
+    CHECK(reinterpret_cast<const char *>(prism::g_single.g.ticket) == ws + L.barrier_offset + 4096 * 8 + 8);
+    CHECK(reinterpret_cast<const char *>(prism::g_single.g.go) == ws + L.barrier_offset + 33024);
+    CHECK(reinterpret_cast<const char *>(prism::g_single.g.tau_words) == ws + L.barrier_offset + 37120);
+    CHECK(L.total_bytes >= L.barrier_offset + 37120 + 32 * 16);
+    const uint64_t tag1 = prism::g_single.g.tag;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_OK);
+    CHECK(prism::g_single.g.tag != tag1 && (prism::g_single.g.tag & 1));  // a new value per call
+    c.flags = PRISM_EST_SINGLE_LAUNCH | PRISM_EST_KEEP_LOGITS;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_OK);
+    c.flags = PRISM_EST_SINGLE_LAUNCH;
+    CHECK(est(tensor(131073, 32), tensor(131073, 8), c, mask(131073, 32), 1) == PRISM_ERR_UNSUPPORTED);
+    c.band_mode = PRISM_BANDS_ADAPTIVE;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_ERR_UNSUPPORTED);
+    c.band_mode = PRISM_BANDS_STATIC;
+    c.flags = 4;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_ERR_CONFIG);
+  }
   CHECK(attn(tensor(131072, 32), tensor(131072, 8), tensor(131072, 8), mask(131072, 32), tensor(131072, 32)) == PRISM_OK);
 
   // NULLs everywhere
@@ -155,7 +189,7 @@ int main() {
       c = cfg(); c.block_size = x; est(q, k, c, m, 3);
       c = cfg(); c.tau_mode = x; est(q, k, c, m, 3);
       c = cfg(); c.rope_layout = x; est(q, k, c, m, 3);
-      c = cfg(); c.flags = x; est(q, k, c, m, 3);
+      c = cfg(); c.flags = x; est(q, k, c, m, (x & PRISM_EST_SINGLE_LAUNCH) ? 1 : 3);
       c = cfg(); c.merge = x; est(q, k, c, m, 3);
       c = cfg(); c.band_mode = x; est(q, k, c, m, x == PRISM_BANDS_ADAPTIVE ? 4 : 3);
       prism_mask_t mm = m; mm.format = x; est(q, k, cfg(), mm, 3);

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.prism_abi_version() == 6
+    assert lib.prism_abi_version() == 7
     for s in range(11):
         assert lib.prism_status_str(s).decode() not in ("", "unknown status")
     assert lib.prism_status_str(42).decode() == "unknown status"
@@ -116,7 +116,7 @@ def test_workspace_layout(lib):
                                         ctypes.byref(L))
     assert L.logits_plane == 64  # 8 rows of 8 floats
     # unknown flag bits are rejected
-    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(flags=2))) == 0
+    assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(flags=4))) == 0
     # past 1024 blocks the logits always pass through the workspace
     q2, k2 = tensor(seq=1025 * 128, heads=2), tensor(seq=1025 * 128, heads=1)
     lib.prism_estimate_workspace_layout(ctypes.byref(q2), ctypes.byref(k2), ctypes.byref(cfg()), ctypes.byref(L))
@@ -184,6 +184,11 @@ E = _abi
     (dict(q=tensor(heads=4096, seq=8192 * 128), k=tensor(heads=8, seq=8192 * 128),
           m=mask(seq=8192 * 128, heads=4096)), E.ERR_UNSUPPORTED),
     (dict(m=mask(format=1, data=FAKE + 2)), E.ERR_ALIGN),
+    # the single persistent launch: fused scores (up to 1024 blocks) and static bands only
+    (dict(q=tensor(seq=1025 * 128), k=tensor(seq=1025 * 128, heads=8), m=mask(seq=1025 * 128),
+          c=cfg(flags=E.EST_SINGLE_LAUNCH)), E.ERR_UNSUPPORTED),
+    (dict(c=cfg(flags=E.EST_SINGLE_LAUNCH, band_mode=1)), E.ERR_UNSUPPORTED),
+    (dict(c=cfg(flags=E.EST_SINGLE_LAUNCH | 8)), E.ERR_CONFIG),
 ])
 def test_estimate_rejects(lib, case, expect):
     args = dict(q=tensor(), k=tensor(heads=8), c=cfg(), m=mask())
@@ -349,3 +354,26 @@ def test_adaptive_layout_sections(lib):
     for merge in (1, 2):
         assert lib.prism_estimate_workspace_bytes(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg(merge=merge))) \
             == static_total
+
+
+def test_single_launch_layout_section(lib):
+    """the single persistent launch adds a barrier section (4096 uint64 barrier words,
+    the status word, a task counter, the go word, two words per query head) at the
+    end of the workspace; nothing else moves"""
+    q, k = tensor(seq=1000, heads=32), tensor(seq=1000, heads=8)
+    L, L1 = PrismWorkspaceLayout(), PrismWorkspaceLayout()
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(cfg()),
+                                               ctypes.byref(L)) == 0
+    assert L.barrier_offset == L.total_bytes  # empty section
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k),
+                                               ctypes.byref(cfg(flags=E.EST_SINGLE_LAUNCH)), ctypes.byref(L1)) == 0
+    for f in ("qbar_offset", "kbar_offset", "qsq_offset", "ksq_offset", "tau_offset", "logits_offset",
+              "spectrum_offset", "split_offset", "barrier_offset"):
+        assert getattr(L1, f) == getattr(L, f), f
+    # 4096 barrier words, status and task counter (256 bytes), 16 go words 256 bytes apart,
+    # 2 words per query head; rounded up to 256
+    assert L1.total_bytes == L.total_bytes + (4096 * 8 + 256 + 16 * 256 + 32 * 16 + 255) // 256 * 256
+    keep = cfg(flags=E.EST_SINGLE_LAUNCH | E.EST_KEEP_LOGITS)
+    assert lib.prism_estimate_workspace_layout(ctypes.byref(q), ctypes.byref(k), ctypes.byref(keep),
+                                               ctypes.byref(L1)) == 0
+    assert L1.logits_plane == 64 and L1.barrier_offset >= L1.logits_offset + 32 * 2 * 64 * 4

@@ -1,0 +1,122 @@
+"""GPU: the estimator as one persistent launch (PRISM_EST_SINGLE_LAUNCH) against
+the three-launch path, through the C ABI. Both run the same arithmetic in the
+same order, so the masks and every workspace intermediate (block means,
+segment energies, temperatures, logits when kept) must agree bit for bit; the
+masks are also held to the oracle under the parity rule of tests/parity.py.
+The barrier words start from garbage (a workspace filled with 0xFF) and from
+the previous call's values (two calls in a row on one workspace); the
+barrier's status word must stay 0."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_attention_band_amd as prism  # noqa: E402
+from synth import WORKLOADS, make_qkv  # noqa: E402
+from tests.parity import compare_masks, oracle_estimate_heads, to_device  # noqa: E402
+from tests.test_parity_gpu import SMALL, cfg_of  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    prism.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# every small case the single launch takes: static bands, at most 1024 blocks
+SINGLE = [n for n, (base, over, cov, _, _) in SMALL.items()
+          if cov.get("band_mode", "static") == "static"
+          and (WORKLOADS[base].scaled(**over).seq + 127) // 128 <= 1024]
+
+
+def sections(ws, L, with_logits):
+    names = ["qbar", "kbar", "qsq", "ksq", "tau"] + (["logits"] if with_logits else [])
+    ends = {"qbar": L.kbar_offset, "kbar": L.qsq_offset, "qsq": L.ksq_offset, "ksq": L.tau_offset,
+            "tau": L.logits_offset, "logits": L.spectrum_offset}
+    return {n: ws[getattr(L, n + "_offset"): ends[n]].cpu().numpy() for n in names}
+
+
+def run_both(qd, kd, cfg, bits=False, calls=1):
+    """(mask, sections, status) of the three-launch path and of the single launch"""
+    out = []
+    for single in (False, True):
+        c = prism.EstimatorConfig(**{**cfg.__dict__, "single_launch": single})
+        L = prism.workspace_layout(qd, kd, c)
+        ws = torch.full((L.total_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+        if single:
+            st = L.barrier_offset + 4096 * 8
+            ws[st: st + 4] = 0  # the library never clears the status word
+        nb = int(L.nb)
+        shape = (qd.shape[0], qd.shape[2], nb, (nb + 31) // 32 if bits else nb)
+        m = None
+        for _ in range(calls):
+            m = torch.full(shape, 7, dtype=torch.int32 if bits else torch.uint8, device="cuda")
+            prism.estimate(qd, kd, c, workspace=ws, mask_out=m)
+        torch.cuda.synchronize()
+        status = int(ws[L.barrier_offset + 4096 * 8: L.barrier_offset + 4096 * 8 + 4].view(torch.int32).item()) \
+            if single else 0
+        out.append((m.cpu().numpy(), sections(ws, L, cfg.keep_logits), status))
+    return out
+
+
+def assert_same(ref, single, name):
+    (m0, s0, _), (m1, s1, status) = ref, single
+    assert status == 0, f"{name}: a workgroup gave up at the barrier"
+    assert np.array_equal(m0, m1), f"{name}: masks differ in {int((m0 != m1).sum())} entries"
+    for k in s0:
+        assert np.array_equal(s0[k], s1[k]), f"{name}: workspace section {k} differs"
+
+
+@pytest.mark.parametrize("name", SINGLE)
+def test_single_launch_equals_three_launches(name):
+    base, over, cov, layout, rope_layout = SMALL[name]
+    w = WORKLOADS[base].scaled(**over)
+    say(f"[single] {name}: seq={w.seq} hq={w.hq} hkv={w.hkv} b={w.batch} {w.dtype} {layout} {cov}")
+    q, k, _ = make_qkv(w, rope_layout=rope_layout, with_v=False)
+    qd, kd = to_device(q, w.dtype, layout), to_device(k, w.dtype, layout)
+    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout})
+    ref, single = run_both(qd, kd, cfg)
+    assert_same(ref, single, name)
+    orc = oracle_estimate_heads(q, k, w.dtype, block=w.block, d_high=cfg.d_high, d_low=cfg.d_low, p=cfg.p,
+                                causal=cfg.causal, rope_layout=rope_layout, tau_mode=cfg.tau_mode, merge=cfg.merge)
+    res = compare_masks(single[0], orc, cfg.p, cfg.causal, merge=cfg.merge)
+    assert res["unexcused"] == 0, (name, res)
+
+
+@pytest.mark.parametrize("name,bits,keep,calls", [
+    ("gqa4_ragged", True, False, 1),       # bit-packed rows
+    ("gqa4_ragged", False, True, 1),       # logits kept in the workspace as well
+    ("mha_batch2", False, False, 3),       # the barrier words hold the previous call's values
+])
+def test_single_launch_options(name, bits, keep, calls):
+    base, over, cov, layout, rope_layout = SMALL[name]
+    w = WORKLOADS[base].scaled(**over)
+    say(f"[single options] {name}: bits={bits} keep_logits={keep} calls={calls}")
+    q, k, _ = make_qkv(w, rope_layout=rope_layout, with_v=False)
+    qd, kd = to_device(q, w.dtype, layout), to_device(k, w.dtype, layout)
+    cfg = cfg_of(w, **{**cov, "rope_layout": rope_layout, "keep_logits": keep})
+    ref, single = run_both(qd, kd, cfg, bits=bits, calls=calls)
+    assert_same(ref, single, name)
+
+
+@pytest.mark.parametrize("wname", ["llama3_8b_128k", "llama3_70b_share_128k", "llama3_8b_32k"])
+def test_single_launch_full_size(wname):
+    """the full layers: every head's mask and intermediates, bit for bit"""
+    w = WORKLOADS[wname]
+    say(f"[single full] {wname}: seq={w.seq} hq={w.hq} hkv={w.hkv}")
+    q, k, _ = make_qkv(w, with_v=False)
+    qd, kd = to_device(q, w.dtype), to_device(k, w.dtype)
+    del q, k
+    ref, single = run_both(qd, kd, cfg_of(w))
+    assert_same(ref, single, wname)
