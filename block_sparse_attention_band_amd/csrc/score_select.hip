@@ -1008,13 +1008,13 @@ __device__ __forceinline__ bool waited_too_long(uint64_t t0) {
   return __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
 }
 
-// One round of the grid barrier: every workgroup sets its barrier word to
+// One pass of the grid barrier: every workgroup sets its barrier word to
 // `v`; workgroup 0 waits until every word holds v, then sets the go words to
 // v; each of the others waits on one go word (one thread polling, about once
 // a microsecond; kGoCopies copies on separate lines, so no one memory channel
 // takes every poll). `before_go` runs in workgroup 0 between the two.
 template <typename BeforeGo>
-__device__ __forceinline__ void barrier_round(const SingleArgs &g, uint64_t v, uint64_t t0, BeforeGo &&before_go) {
+__device__ __forceinline__ void barrier_pass(const SingleArgs &g, uint64_t v, uint64_t t0, BeforeGo &&before_go) {
   if (threadIdx.x == 0) __hip_atomic_store(g.slots + blockIdx.x, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (blockIdx.x == 0) {
     for (;;) {
@@ -1044,21 +1044,22 @@ __device__ __forceinline__ void barrier_round(const SingleArgs &g, uint64_t v, u
   __syncthreads();
 }
 
-// The grid barrier after the pooling, in two rounds. Publishing to the other
+// The grid barrier after the pooling, in two passes. Publishing to the other
 // XCDs takes a write-back of this XCD's L2 (the release at device scope);
 // issued by a workgroup while others still stream their pooling reads, those
-// write-backs slowed the reads by 13% (measured). So: round 1 only says that
-// this workgroup's stores have reached its L2 (tag); once every workgroup is
-// there, each writes its L2 back and says so (tag + 1), and after round 2
-// every workgroup invalidates its caches (the acquire at device scope).
+// write-backs slowed the reads by 13% (measured). So the first pass only
+// says that this workgroup's stores have reached its L2 (tag); once every
+// workgroup is there, each writes its L2 back and says so (tag + 1), and
+// after the second pass every workgroup invalidates its caches (the acquire
+// at device scope).
 __device__ __forceinline__ void grid_barrier(const SingleArgs &g) {
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have reached the L2
   __syncthreads();
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-  barrier_round(g, g.tag, t0, [] {});
+  barrier_pass(g, g.tag, t0, [] {});
   if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  barrier_round(g, g.tag + 1, t0, [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); });
+  barrier_pass(g, g.tag + 1, t0, [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent"); });
   if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __syncthreads();
 }
