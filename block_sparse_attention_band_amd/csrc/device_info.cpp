@@ -27,6 +27,13 @@ hipError_t stream_device(hipStream_t s, int *dev) {
   return hipStreamGetDevice(s, dev);
 }
 
+hipError_t stream_capturing(hipStream_t s, bool *capturing) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &st);
+  *capturing = st != hipStreamCaptureStatusNone;
+  return e;
+}
+
 hipError_t device_cu_count(int dev, int *cus) {
   if (dev < 0 || dev >= kMaxDevices) return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
   std::call_once(g_once[dev], [dev] {

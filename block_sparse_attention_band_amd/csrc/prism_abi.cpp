@@ -305,6 +305,10 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
   sc.h0 = tp.h0 = 0;
   sc.nh = tp.nh = ta.hq;
   if (cfg->flags & PRISM_EST_SINGLE_LAUNCH) {
+    // One launch's tag baked into a captured graph would be replayed: the
+    // barrier words would already hold it. Graph capture takes the default.
+    bool capturing = true;
+    if (prism::stream_capturing(s, &capturing) != hipSuccess || capturing) return PRISM_ERR_UNSUPPORTED;
     prism::SingleParams P;
     P.pa = pa;
     P.ta = ta;
@@ -316,6 +320,11 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
     P.g.go = reinterpret_cast<uint64_t *>(ws + L.barrier_offset + prism::kSingleGoOffset);
     P.g.tau_words = reinterpret_cast<uint64_t *>(ws + L.barrier_offset + prism::kSingleTauOffset);
     P.g.tag = barrier_tag();
+    // Longest device-side wait: 10 s plus the pooling pass at 0.5 TB/s (a
+    // twelfth of the part's read rate), so only a broken protocol reaches it.
+    const double pooled = (double)q->batch * (double)q->seq * (double)(q->heads + k->heads) * kHeadDim *
+                          (double)(fp32 ? 4 : 2);
+    P.g.wait_ticks = (uint64_t)(1e8 * (10.0 + pooled / 5e11));
     P.batch = (int)q->batch;
     const hipError_t e = prism::launch_estimate_single(P, fp32, prism::kSingleMaxWgs, s);
     return e == hipSuccess ? PRISM_OK : PRISM_ERR_LAUNCH;

@@ -120,6 +120,7 @@ struct SingleArgs {
   uint64_t *go;            // kGoCopies words kGoStride apart, := tag once every workgroup has reached the barrier
   uint64_t *tau_words;     // [batch * Hq][2]: tau_high, tau_low as (tag low 32 bits << 32) | float bits
   uint64_t tag;            // this call's value, unlike any earlier call's (odd)
+  uint64_t wait_ticks;     // longest wait, in ticks of the 100 MHz real-time counter
 };
 constexpr int kSingleMaxWgs = 4096;  // barrier words in the workspace
 constexpr int kGoCopies = 16, kGoStride = 32;  // go words: 16 copies, 256 bytes apart
@@ -167,6 +168,8 @@ int enqueue_estimate(const prism_tensor_t *q, const prism_tensor_t *k, const pri
 
 // The device a stream belongs to (the current device for the null stream).
 hipError_t stream_device(hipStream_t s, int *dev);
+// Whether work enqueued on the stream now is being captured into a graph.
+hipError_t stream_capturing(hipStream_t s, bool *capturing);
 // Compute units of a device, queried once per device and cached.
 hipError_t device_cu_count(int dev, int *cus);
 // Workgroups of `threads` threads of kernel f resident per CU (on the current

@@ -937,10 +937,10 @@ void score_topp_kernel(ScoreArgs a, TopPArgs t) {
 //    temperatures are read from their words, then score_topp_strip.
 // No word has to start at zero (the counter is set by workgroup 0 before the
 // barrier; the other words are recognised by the tag), so the call needs no
-// clearing launch. Every wait gives up after about 4 s (then `status` := 1
-// and the call's outputs are not valid).
+// clearing launch. Every wait gives up after g.wait_ticks of the 100 MHz
+// real-time counter (then `status` := 1 and the call's outputs are not
+// valid); the host sizes it far above the pooling pass's duration.
 constexpr int kSingleSlots = 6;
-constexpr uint64_t kWaitTicks = 400000000ull;  // s_memrealtime ticks at 100 MHz: 4 s
 
 template <bool FP32>
 struct SinglePoolLds {
@@ -1004,8 +1004,8 @@ __device__ __forceinline__ void single_pool(const PoolArgs &a, int batch, unsign
   }
 }
 
-__device__ __forceinline__ bool waited_too_long(uint64_t t0) {
-  return __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks;
+__device__ __forceinline__ bool waited_too_long(const SingleArgs &g, uint64_t t0) {
+  return __builtin_amdgcn_s_memrealtime() - t0 > g.wait_ticks;
 }
 
 // One pass of the grid barrier: every workgroup sets its barrier word to
@@ -1022,7 +1022,7 @@ __device__ __forceinline__ void barrier_pass(const SingleArgs &g, uint64_t v, ui
       for (int w = threadIdx.x; w < (int)gridDim.x; w += blockDim.x)
         ok &= __hip_atomic_load(g.slots + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == v;
       if (__syncthreads_and(ok)) break;
-      if (__syncthreads_or(threadIdx.x == 0 && waited_too_long(t0))) {
+      if (__syncthreads_or(threadIdx.x == 0 && waited_too_long(g, t0))) {
         if (threadIdx.x == 0) __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -1034,7 +1034,7 @@ __device__ __forceinline__ void barrier_pass(const SingleArgs &g, uint64_t v, ui
   } else if (threadIdx.x == 0) {
     const uint64_t *go = g.go + (blockIdx.x % kGoCopies) * kGoStride;
     while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != v) {
-      if (waited_too_long(t0)) {
+      if (waited_too_long(g, t0)) {
         __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
@@ -1070,12 +1070,12 @@ __device__ __forceinline__ uint64_t tagged(uint32_t tag32, float v) {
 }
 
 // word i of the published temperatures, once it carries the tag (1 after
-// about 4 s without it, and status := 1)
+// the wait limit without it, and status := 1)
 __device__ __forceinline__ float wait_tau(const SingleArgs &g, int i, uint32_t tag32) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   uint64_t v;
   while (((v = __hip_atomic_load(g.tau_words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 32) != tag32) {
-    if (waited_too_long(t0)) {
+    if (waited_too_long(g, t0)) {
       __hip_atomic_store(g.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return 1.f;
     }

@@ -249,8 +249,9 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
     kdma[u] = row * (int)kss + (kslot(slot, row) << 4);
     vdma[u] = row * (int)vss + (vslot(slot, row) << 4);
   }
-  auto dma_sub = [&](int n, uint8_t *Kd, uint8_t *Vd) {
-    const int kv0 = (int)(__builtin_amdgcn_readfirstlane((int)blist[n >> 1]) & kBlockBits) * kBlock + (n & 1) * kSub;
+  // sub-tile n, of the block whose list entry is ent (uniform)
+  auto dma_sub = [&](int n, uint32_t ent, uint8_t *Kd, uint8_t *Vd) {
+    const int kv0 = (int)(ent & kBlockBits) * kBlock + (n & 1) * kSub;
     // a sub-tile starting past the sequence end (the second half of a last
     // block of at most 64 tokens) is never computed; its rows read row N - 1
     const int kb0 = min(kv0, N - 1);
@@ -302,8 +303,7 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
   float m_ref = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
 
-  auto compute = [&](int n, const uint8_t *Kb, const uint8_t *Vb) {
-    const uint32_t ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)blist[n >> 1]);
+  auto compute = [&](int n, uint32_t ent, const uint8_t *Kb, const uint8_t *Vb) {
     const int j = (int)(ent & kBlockBits);
     const int kv0 = j * kBlock + (n & 1) * kSub;
     const bool diag = a.causal && j == i;
@@ -408,21 +408,30 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
   for (int cb = 0;;) {
     const int nsel = nsel_s;
     const int nsub = 2 * nsel;
+    // Block list entries (uniform): e_cur is the block of sub-tiles n and
+    // n + 1; the next block's entry is read from LDS a whole sub-tile ahead,
+    // so its latency hides behind the fragment reads instead of stalling the
+    // wave twice per sub-tile between the barrier and its next MFMA (a
+    // per-wave timeline measured ~300 cycles per round trip there).
+    uint32_t e_cur = nsel > 0 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)blist[0]) : 0u;
     if (nsub > 0) {
-      dma_sub(0, K0, V0);
+      dma_sub(0, e_cur, K0, V0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     __syncthreads();
     for (int n = 0; n < nsub; n += 2) {
-      if (n + 1 < nsub) dma_sub(n + 1, K1, V1);
-      compute(n, K0, V0);
+      const int e_raw = (n >> 1) + 1 < nsel ? (int)blist[(n >> 1) + 1] : 0;
+      if (n + 1 < nsub) dma_sub(n + 1, e_cur, K1, V1);
+      compute(n, e_cur, K0, V0);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       if (n + 1 >= nsub) break;
-      if (n + 2 < nsub) dma_sub(n + 2, K0, V0);
-      compute(n + 1, K1, V1);
+      const uint32_t e_nxt = (uint32_t)__builtin_amdgcn_readfirstlane(e_raw);
+      if (n + 2 < nsub) dma_sub(n + 2, e_nxt, K0, V0);
+      compute(n + 1, e_cur, K1, V1);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
+      e_cur = e_nxt;
     }
     // rows longer than kListCap blocks: the next part of the mask row (every
     // wave has passed the last barrier, so blist is free)

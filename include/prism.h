@@ -155,8 +155,10 @@ typedef enum { PRISM_BANDS_STATIC = 0, PRISM_BANDS_ADAPTIVE = 1 } prism_band_mod
  * barrier_offset); they are tagged with a value new to each call, so any
  * prior contents are fine (a stale word matching that tag by chance, odds
  * 2^-32 per word, would corrupt the call). The status word becomes 1 if a
- * workgroup waited longer than about 4 s (the call's outputs are then not
- * valid); the library never clears it. */
+ * workgroup waited longer than 10 s plus the time to read Q and K at
+ * 0.5 TB/s (the call's outputs are then not valid); the library never clears
+ * it. Not for HIP graph capture (a captured call would replay one tag):
+ * PRISM_ERR_UNSUPPORTED on a capturing stream. */
 #define PRISM_EST_KEEP_LOGITS 1
 #define PRISM_EST_SINGLE_LAUNCH 2
 

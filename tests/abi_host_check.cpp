@@ -31,6 +31,8 @@ hipError_t launch_estimate_single(const SingleParams &p, int, int grid_cap, hipS
 hipError_t launch_attn_bf16(const AttnArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t launch_attn_fp32(const AttnArgs &, hipStream_t) { ++g_launches; return hipSuccess; }
 hipError_t stream_device(hipStream_t, int *dev) { *dev = 0; return hipSuccess; }
+bool g_capturing = false;  // what the capture query reports
+hipError_t stream_capturing(hipStream_t, bool *capturing) { *capturing = g_capturing; return hipSuccess; }
 hipError_t device_cu_count(int, int *cus) { *cus = 256; return hipSuccess; }
 }  // namespace prism
 
@@ -133,6 +135,16 @@ int main() {
     c.band_mode = PRISM_BANDS_STATIC;
     c.flags = 4;
     CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_ERR_CONFIG);
+    // the longest device wait: 10 s plus Q and K (2.7 GB here) at 0.5 TB/s, in 100 MHz ticks
+    c.flags = PRISM_EST_SINGLE_LAUNCH;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_OK);
+    CHECK(prism::g_single.g.wait_ticks > 1000000000ull && prism::g_single.g.wait_ticks < 1100000000ull);
+    // a capturing stream: refused, nothing enqueued (the default path is capturable)
+    prism::g_capturing = true;
+    CHECK(est(q, k, c, mask(131072, 32), 1) == PRISM_ERR_UNSUPPORTED);
+    c.flags = 0;
+    CHECK(est(q, k, c, mask(131072, 32), 3) == PRISM_OK);
+    prism::g_capturing = false;
   }
   CHECK(attn(tensor(131072, 32), tensor(131072, 8), tensor(131072, 8), mask(131072, 32), tensor(131072, 32)) == PRISM_OK);
 

@@ -120,3 +120,46 @@ def test_single_launch_full_size(wname):
     del q, k
     ref, single = run_both(qd, kd, cfg_of(w))
     assert_same(ref, single, wname)
+
+
+def test_single_launch_many_heads_uncached_temperatures():
+    """more query heads (batch x Hq = 576) than a workgroup keeps temperatures
+    for in LDS: each strip reads its head's published words instead"""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=700, hq=64, hkv=8, batch=9)
+    say(f"[single many heads] seq={w.seq} hq={w.hq} hkv={w.hkv} b={w.batch}")
+    q, k, _ = make_qkv(w, with_v=False)
+    qd, kd = to_device(q, w.dtype), to_device(k, w.dtype)
+    ref, single = run_both(qd, kd, cfg_of(w))
+    assert_same(ref, single, "many_heads")
+
+
+def test_single_launch_refused_under_graph_capture():
+    """a captured call would replay one barrier tag: the flag is refused on a
+    capturing stream (nothing enqueued), and the default path still captures"""
+    w = WORKLOADS["llama3_8b_32k"].scaled(seq=2000, hq=4, hkv=1)
+    q, k, _ = make_qkv(w, with_v=False)
+    qd, kd = to_device(q, w.dtype), to_device(k, w.dtype)
+    cfg1 = cfg_of(w, single_launch=True)
+    ws = prism.new_workspace(qd, kd, cfg1)
+    mask = torch.empty((1, w.hq, w.nb, w.nb), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    err = None
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            try:
+                prism.estimate(qd, kd, cfg1, workspace=ws, mask_out=mask)
+            except prism.PrismError as e:
+                err = e
+            prism.estimate(qd, kd, cfg_of(w), workspace=ws, mask_out=mask)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert err is not None and err.status == prism._abi.ERR_UNSUPPORTED
+    mask.fill_(9)
+    g.replay()
+    torch.cuda.synchronize()
+    ref = prism.estimate(qd, kd, cfg1)  # eager single launch: the same bytes
+    torch.cuda.synchronize()
+    assert torch.equal(mask, ref)
