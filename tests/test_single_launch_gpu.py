@@ -163,3 +163,36 @@ def test_single_launch_refused_under_graph_capture():
     ref = prism.estimate(qd, kd, cfg1)  # eager single launch: the same bytes
     torch.cuda.synchronize()
     assert torch.equal(mask, ref)
+
+
+def test_single_launch_two_streams_concurrent():
+    """two single-launch calls in flight at once on two streams (own workspaces):
+    each grid must become resident as a whole (cooperative launch), so neither
+    waits on workgroups the other holds; both give the three-launch bytes and
+    leave their status words at 0"""
+    ws_ = [WORKLOADS["llama3_8b_32k"].scaled(seq=40000, hq=32, hkv=8),
+           WORKLOADS["qwen3_8b_64k"].scaled(seq=30000, hq=32, hkv=8)]
+    data = []
+    for w in ws_:
+        q, k, _ = make_qkv(w, with_v=False)
+        qd, kd = to_device(q, w.dtype), to_device(k, w.dtype)
+        ref = prism.estimate(qd, kd, cfg_of(w))
+        cfg1 = cfg_of(w, single_launch=True)
+        L = prism.workspace_layout(qd, kd, cfg1)
+        ws = torch.zeros((L.total_bytes,), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        data.append((qd, kd, cfg1, ref.clone(), ws, L))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (qd, kd, cfg1, _, ws, L), st in zip(data, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            m = torch.empty_like(data[len(outs)][3])
+            for _ in range(4):
+                prism.estimate(qd, kd, cfg1, workspace=ws, mask_out=m)
+            outs.append(m)
+    torch.cuda.synchronize()
+    for m, (qd, kd, cfg1, ref, ws, L) in zip(outs, data):
+        status = int(ws[L.barrier_offset + 4096 * 8: L.barrier_offset + 4096 * 8 + 4].view(torch.int32).item())
+        assert status == 0
+        assert torch.equal(m, ref)
