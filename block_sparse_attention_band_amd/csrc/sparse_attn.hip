@@ -13,8 +13,10 @@
 //   * Keys and values stream in sub-tiles of 64 tokens through two LDS
 //     buffers by direct global-to-LDS loads (buffer_load ... lds, no staging
 //     registers): the next sub-tile's loads are in flight while the current
-//     one is computed. Rows sit in LDS with XOR-swizzled 16-byte chunks so
-//     every operand read is free of bank conflicts.
+//     one is computed, issued between its S MFMAs. Rows sit in LDS with
+//     XOR-swizzled 16-byte chunks so every operand read is free of bank
+//     conflicts; rows past the sequence end lie outside the buffer range and
+//     read as zeros.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q held in registers. Key
 //     rows are fed to the MFMA in a permuted order chosen so that each lane's
 //     16 accumulator registers per 32-key tile hold, for k-step v, eight
@@ -238,7 +240,6 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
   const int64_t kss = a.k.ss * 2, vss = a.v.ss * 2;
   const char *kbase = static_cast<const char *>(a.k.data) + ((int64_t)b * a.k.sb + (int64_t)g * a.k.sh) * 2;
   const char *vbase = static_cast<const char *>(a.v.data) + ((int64_t)b * a.v.sb + (int64_t)g * a.v.sh) * 2;
-  const uint32_t krec = (uint32_t)((kSub - 1) * kss + 256), vrec = (uint32_t)((kSub - 1) * vss + 256);
 
   // DMA instruction u of wave w fills LDS bytes [(NW u + w) * 1024, +1024):
   // tile rows 4(NW u + w) .. +3, lane -> (row + lane/16, slot lane%16)
@@ -249,30 +250,31 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
     kdma[u] = row * (int)kss + (kslot(slot, row) << 4);
     vdma[u] = row * (int)vss + (vslot(slot, row) << 4);
   }
-  // sub-tile n, of the block whose list entry is ent (uniform)
-  auto dma_sub = [&](int n, uint32_t ent, uint8_t *Kd, uint8_t *Vd) {
+  // The loads of one sub-tile: dma_prep sets their buffer resources (scalar
+  // work only), dma_one(u) issues load u (K for u < DPW, then V). A
+  // sub-tile's record range ends with the sequence's last row, so rows past
+  // the sequence end read as zeros: their scores are masked and their
+  // probabilities are exactly 0. A sub-tile that is not needed (live false:
+  // none follows the last) gets an empty range and only zero-fills the idle
+  // buffer.
+  i32x4 pk = {0, 0, 0, 0}, pv = {0, 0, 0, 0};
+  uint8_t *pK = K0, *pV = V0;
+  auto dma_prep = [&](int n, uint32_t ent, uint8_t *Kd, uint8_t *Vd, bool live) {
     const int kv0 = (int)(ent & kBlockBits) * kBlock + (n & 1) * kSub;
-    // a sub-tile starting past the sequence end (the second half of a last
-    // block of at most 64 tokens) is never computed; its rows read row N - 1
-    const int kb0 = min(kv0, N - 1);
-    const i32x4 krs = make_rsrc(kbase + kb0 * kss, krec);
-    const i32x4 vrs = make_rsrc(vbase + kb0 * vss, vrec);
-    if (kv0 + kSub <= N) {
+    const int rows = live ? min(kSub, N - kv0) : 0;  // <= 0 past the sequence end
+    const int kv = live ? kv0 : 0;
+    pk = make_rsrc(kbase + kv * kss, rows > 0 ? (uint32_t)((rows - 1) * kss + 256) : 0u);
+    pv = make_rsrc(vbase + kv * vss, rows > 0 ? (uint32_t)((rows - 1) * vss + 256) : 0u);
+    pK = Kd;
+    pV = Vd;
+  };
+  auto dma_one = [&](int u) {
+    if (u < DPW) dma16(pk, pK + (NW * u + wave) * 1024, kdma[u], 0);
+    else dma16(pv, pV + (NW * (u - DPW) + wave) * 1024, vdma[u - DPW], 0);
+  };
+  auto dma_all = [&]() {
 #pragma unroll
-      for (int u = 0; u < DPW; ++u) dma16(krs, Kd + (NW * u + wave) * 1024, kdma[u], 0);
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) dma16(vrs, Vd + (NW * u + wave) * 1024, vdma[u], 0);
-    } else {
-      // ragged end: rows past the sequence re-read the last row; their
-      // scores are masked and their probabilities are exactly 0
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) {
-        const int row = 4 * (NW * u + wave) + (lane >> 4), slot = lane & 15;
-        const int r = min(kv0 + row, N - 1) - kb0;  // 0 <= r < kSub
-        dma16(krs, Kd + (NW * u + wave) * 1024, r * (int)kss + (kslot(slot, row) << 4), 0);
-        dma16(vrs, Vd + (NW * u + wave) * 1024, r * (int)vss + (vslot(slot, row) << 4), 0);
-      }
-    }
+    for (int u = 0; u < 2 * DPW; ++u) dma_one(u);
   };
 
   // LDS read offsets. K (A operand of S^T): lane feeds key row 32t + pm,
@@ -307,9 +309,15 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
     const int j = (int)(ent & kBlockBits);
     const int kv0 = j * kBlock + (n & 1) * kSub;
     const bool diag = a.causal && j == i;
-    // a block this wave's head did not select (the other head's), a whole
-    // sub-tile after every query of this wave, or one past the sequence end
-    if (!(ent & myflag) || (diag && kv0 > i * kBlock + wq * 32 + 31) || kv0 >= N) return;
+    // The head-pair kernel skips a block this wave's head did not select
+    // (the other head's), a whole sub-tile after every query of this wave
+    // and one past the sequence end. The single-head kernel computes the
+    // last two as fully masked sub-tiles (probabilities exactly 0; two waves
+    // on the diagonal block, once per row): its compute carries the next
+    // sub-tile's loads, which every wave must issue.
+    if constexpr (PAIR) {
+      if (!(ent & myflag) || (diag && kv0 > i * kBlock + wq * 32 + 31) || kv0 >= N) return;
+    }
     // All 16 K fragments of the sub-tile are requested before the first
     // MFMA, and all 16 V^T fragments right after the last S MFMA (they are in
     // flight during the softmax): each MFMA then waits for at most one LDS
@@ -328,9 +336,25 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
 #pragma unroll
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][s], qf[s], sacc[t], 0, 0, 0);
+      if constexpr (!PAIR) dma_one(s);
+    }
+    if constexpr (!PAIR) {
+      // Single-head kernel: the next sub-tile's eight loads go out one after
+      // every two S MFMAs, so the wave waits for the load path (which the
+      // workgroup's 32 loads keep busy for ~500 cycles) while its own MFMAs
+      // run, instead of all at once after the barrier; the V^T reads follow
+      // the twelfth MFMA.
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        if (s == 5) __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // DS read
+        if (s == 6) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      }
+    }
     bf16x8 vf[4][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -415,20 +439,28 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
     // per-wave timeline measured ~300 cycles per round trip there).
     uint32_t e_cur = nsel > 0 ? (uint32_t)__builtin_amdgcn_readfirstlane((int)blist[0]) : 0u;
     if (nsub > 0) {
-      dma_sub(0, e_cur, K0, V0);
+      dma_prep(0, e_cur, K0, V0, true);
+      dma_all();
       __builtin_amdgcn_s_waitcnt(0x0F70);
     }
     __syncthreads();
+    // The next sub-tile's loads are prepared before the barrier that
+    // precedes their issue, so the fragment reads follow a barrier at once.
+    // The single-head kernel issues them inside compute (between its S
+    // MFMAs), the head-pair kernel before it.
+    if (nsub > 0) dma_prep(1, e_cur, K1, V1, 1 < nsub);
     for (int n = 0; n < nsub; n += 2) {
       const int e_raw = (n >> 1) + 1 < nsel ? (int)blist[(n >> 1) + 1] : 0;
-      if (n + 1 < nsub) dma_sub(n + 1, e_cur, K1, V1);
+      if constexpr (PAIR) dma_all();
       compute(n, e_cur, K0, V0);
+      const uint32_t e_nxt = (uint32_t)__builtin_amdgcn_readfirstlane(e_raw);
+      dma_prep(n + 2, e_nxt, K0, V0, n + 2 < nsub);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       if (n + 1 >= nsub) break;
-      const uint32_t e_nxt = (uint32_t)__builtin_amdgcn_readfirstlane(e_raw);
-      if (n + 2 < nsub) dma_sub(n + 2, e_nxt, K0, V0);
+      if constexpr (PAIR) dma_all();
       compute(n + 1, e_cur, K1, V1);
+      dma_prep(n + 3, e_nxt, K1, V1, n + 3 < nsub);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       e_cur = e_nxt;
