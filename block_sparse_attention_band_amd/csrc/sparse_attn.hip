@@ -345,14 +345,14 @@ __global__ __launch_bounds__(PAIR ? 512 : 256, PAIR ? 1 : 2) void attn_bf16_kern
       // Single-head kernel: the next sub-tile's eight loads go out one after
       // every two S MFMAs, so the wave waits for the load path (which the
       // workgroup's 32 loads keep busy for ~500 cycles) while its own MFMAs
-      // run, instead of all at once after the barrier; the V^T reads follow
-      // the twelfth MFMA.
+      // run, instead of all at once after the barrier; all V^T reads follow
+      // the last S MFMA (0.8% faster than letting the compiler spread them
+      // over the last few).
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-        if (s == 5) __builtin_amdgcn_sched_group_barrier(0x100, 24, 0);  // DS read
-        if (s == 6) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        if (s == 7) __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);  // DS read
       }
     }
     bf16x8 vf[4][4];
