@@ -458,6 +458,12 @@ ATTN = {
     "xcd_groups": ("llama3_8b_32k", dict(seq=1024, hq=16, hkv=8), 0.8, True, "bshd"),
     "fp32_random": ("tiny_fp32_2k", dict(seq=1500, hq=2, hkv=1), 0.5, True, "bshd"),
     "fp32_noncausal": ("tiny_fp32_2k", dict(seq=600, hq=1, hkv=1), "ones", False, "bshd"),
+    # sequence ends inside the first 64-key sub-tile of a block (the second lies wholly past it),
+    # exactly at a sub-tile boundary, and one token into a new block
+    "short_40": ("llama3_8b_32k", dict(seq=40, hq=2, hkv=1), "ones", True, "bshd"),
+    "short_40_noncausal": ("llama3_8b_32k", dict(seq=40, hq=2, hkv=1), "ones", False, "bshd"),
+    "sub_tile_192": ("llama3_8b_32k", dict(seq=192, hq=2, hkv=1), "ones", True, "bshd"),
+    "one_token_block_257": ("llama3_8b_32k", dict(seq=257, hq=4, hkv=2), 0.7, True, "bshd"),
 }
 
 
