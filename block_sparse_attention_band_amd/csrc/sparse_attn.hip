@@ -54,8 +54,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 // Sequences longer than this many blocks take the head-pair kernel. Measured
-// (Llama-3-8B-shaped layer, density 0.95): the pair kernel is 1.5% slower at
-// 1024 blocks and 0.7% at 3072, 4.4% faster at 4096 and 20% at 8192.
+// (Llama-3-8B-shaped layer, density 0.95, alternating launches on one box):
+// the pair kernel is 1.3% slower at 1024 blocks and 2.1% at 2048 and 3072;
+// on another box 1.7% faster at 3073, 6.2% at 3584 and 7.5% at 4096; ~1.3x
+// faster at 8192, where the one-head kernel is bound by the K/V stream.
 constexpr int kPairMinBlocks = 3072;
 constexpr int kSub = 64;                 // keys per sub-tile
 constexpr int kXcds = 8;
