@@ -87,6 +87,9 @@ SMALL = {
     "tau_pervec_gap": ("llama3_8b_32k", dict(seq=3000, hq=2, hkv=1), dict(tau_mode="pervec", d_high=32, d_low=48),
                        "bshd", "interleaved"),
     "one_block": ("llama3_8b_32k", dict(seq=100, hq=2, hkv=1), {}, "bshd", "interleaved"),
+    # a single token: one block holding one row
+    "one_token": ("llama3_8b_32k", dict(seq=1, hq=2, hkv=1), {}, "bshd", "interleaved"),
+    "one_token_fp32": ("tiny_fp32_2k", dict(seq=1, hq=1, hkv=1), {}, "bshd", "interleaved"),
     "fp32_iid": ("tiny_fp32_2k", dict(seq=1900, hq=2, hkv=1), {}, "bshd", "interleaved"),
     "nb_1100": ("llama3_8b_32k", dict(seq=1100 * 128 - 5, hq=1, hkv=1), {}, "bshd", "interleaved"),
     # the last length whose scores and selection run fused, and the first that goes through the planes
@@ -461,6 +464,8 @@ ATTN = {
     # sequence ends inside the first 64-key sub-tile of a block (the second lies wholly past it),
     # exactly at a sub-tile boundary, and one token into a new block
     "short_40": ("llama3_8b_32k", dict(seq=40, hq=2, hkv=1), "ones", True, "bshd"),
+    "one_token": ("llama3_8b_32k", dict(seq=1, hq=2, hkv=1), "ones", True, "bshd"),
+    "one_token_noncausal_fp32": ("tiny_fp32_2k", dict(seq=1, hq=2, hkv=1), "ones", False, "bshd"),
     "short_40_noncausal": ("llama3_8b_32k", dict(seq=40, hq=2, hkv=1), "ones", False, "bshd"),
     "sub_tile_192": ("llama3_8b_32k", dict(seq=192, hq=2, hkv=1), "ones", True, "bshd"),
     "one_token_block_257": ("llama3_8b_32k", dict(seq=257, hq=4, hkv=2), 0.7, True, "bshd"),
