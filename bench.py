@@ -219,6 +219,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baselines")
     ap.add_argument("--no-machine", action="store_true", help="skip the copy / GEMM microbenchmarks")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--density-sweep", default="",
+                    help="comma-separated block densities: after the line's measurement, time the attention on "
+                         "seeded random causal block masks of these densities (diagonal blocks kept), reported "
+                         "beside the line as `density_sweep`")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB), the "
                          "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -400,6 +404,37 @@ def main():
         result["dense_ms"] = dense
         result["speedup_vs_dense"] = round(best / step_ms, 3)
         log(f"dense: {dense}")
+
+    if args.density_sweep:
+        # context, not the metric: the same attention kernel on random causal block masks (each block
+        # kept with probability d, the diagonal always), read-flushed like the timed steps, median of 3
+        from synth import random_mask
+        dense_own = result.get("dense_ms", {}).get("own_kernel_all_blocks_ms")
+        sweep = []
+        for si, d in enumerate(float(x) for x in args.density_sweep.split(",")):
+            m = random_mask(w.batch, w.hq, nb, d, seed=2000 + si, causal=True)
+            m[..., np.arange(nb), np.arange(nb)] = 1
+            md = torch.from_numpy(m).cuda()
+            del m
+            f, ns = attention_flops(md, w.block, w.head_dim)
+            ts = []
+            for r in range(4):
+                flush()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                e[0].record()
+                prism.block_sparse_attn(qd, kd, vd, md, out=out)
+                e[1].record()
+                torch.cuda.synchronize()
+                if r:
+                    ts.append(e[0].elapsed_time(e[1]))
+            ms = float(np.median(ts))
+            tf = f / (ms * 1e-3) / 1e12
+            sweep.append({"density": round(ns / total_blocks, 4), "attention_ms": round(ms, 3),
+                          "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "speedup_vs_dense_own_kernel": round(dense_own / ms, 3) if dense_own else None})
+            log(f"density sweep: {sweep[-1]}")
+            del md
+        result["density_sweep"] = sweep
 
     if not args.no_machine:
         result["machine"] = machine_microbench()
